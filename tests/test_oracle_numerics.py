@@ -1,0 +1,87 @@
+"""Pins of the oracle's rounding helpers against torch's CPU casts."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import numerics as nx
+
+
+def _all_bf16_values():
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
+    with np.errstate(invalid="ignore"):
+        v = bits.view(torch.bfloat16).float().numpy().astype(np.float64)
+    return v[np.isfinite(v)]
+
+
+def test_bf16_grid_is_fixed_point():
+    v = _all_bf16_values()
+    np.testing.assert_array_equal(nx.to_bf16(v), v)
+
+
+def test_bf16_matches_torch_on_midpoints_and_random():
+    v = _all_bf16_values()
+    v = np.sort(v[v > 0])
+    mids = (v[:-1] + v[1:]) / 2            # exact ties: fp64 holds them
+    rng = np.random.default_rng(0)
+    rnd = rng.normal(size=200_000) * np.exp(rng.uniform(-30, 30, size=200_000))
+    for arr in (mids, -mids, rnd):
+        f32 = arr.astype(np.float32)        # torch casts from fp32
+        ok = f32.astype(np.float64) == arr  # compare only where fp32 is exact
+        ref = torch.from_numpy(f32[ok]).to(torch.bfloat16).float().numpy()
+        np.testing.assert_array_equal(nx.to_bf16(arr[ok]), ref)
+
+
+def test_e4m3_all_codes_and_midpoints():
+    codes = torch.arange(0, 256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    v = codes.float().numpy().astype(np.float64)
+    v = v[np.isfinite(v)]
+    np.testing.assert_array_equal(nx.to_e4m3_sat(v), v)
+    pos = np.sort(np.unique(v[v > 0]))
+    mids = (pos[:-1] + pos[1:]) / 2
+    for arr in (mids, -mids, np.linspace(-448, 448, 100_001)):
+        a32 = arr.astype(np.float32)          # torch casts from fp32
+        ref = torch.from_numpy(a32).to(torch.float8_e4m3fn).float().numpy()
+        np.testing.assert_array_equal(nx.to_e4m3_sat(a32.astype(np.float64)), ref)
+
+
+def test_e4m3_saturates():
+    np.testing.assert_array_equal(nx.to_e4m3_sat([1e9, -1e9, 465.0]), [448.0, -448.0, 448.0])
+
+
+def test_fp8_block_quantiser_properties():
+    rng = np.random.default_rng(1)
+    v = rng.normal(size=(5, 2880)).astype(np.float32) * np.float32(3.0)
+    v[2, 128:256] = 0.0                                   # an all-zero block
+    codes, scales = nx.quantize_fp8_blocks(v)
+    assert scales.shape == (5, 23) and scales.dtype == np.float32   # 22 full blocks + 64 tail
+    assert scales[2, 1] == 1.0 and np.all(codes[2, 128:256] == 0)
+    for b in range(23):
+        blk = codes[:, b * 128:(b + 1) * 128]
+        nz = np.abs(v[:, b * 128:(b + 1) * 128]).max(axis=1) > 0
+        # the block's largest magnitude lands on the top code
+        assert np.all(np.abs(blk[nz]).max(axis=1) == 448.0)
+    deq = nx.dequantize_fp8_blocks(codes, scales)
+    amax = np.repeat(np.abs(v.reshape(5, -1)).max(axis=1, keepdims=True), 2880, axis=1)
+    assert np.all(np.abs(deq - v) <= amax / 448 * 16 * 1.0001)
+
+
+def test_fp8_scale_rule_by_hand():
+    v = np.zeros((1, 136), np.float32)
+    v[0, 0] = 3.5
+    v[0, 5] = -1.0
+    v[0, 130] = 7.0
+    codes, scales = nx.quantize_fp8_blocks(v)
+    assert scales[0, 0] == np.float32(3.5) / np.float32(448)
+    assert scales[0, 1] == np.float32(7.0) / np.float32(448)
+    assert codes[0, 0] == 448.0 and codes[0, 130] == 448.0
+    assert codes[0, 5] == nx.to_e4m3_sat(float(np.float32(-1.0) / scales[0, 0]))
+    assert codes[0, 5] == -128.0                          # -1 / (3.5/448) = -128 exactly
+
+
+def test_round_to_grid_subnormals():
+    # bf16 smallest subnormal is 2^-133; half of it ties to even (zero)
+    assert nx.to_bf16(2.0**-134) == 0.0
+    assert nx.to_bf16(3 * 2.0**-134) == 2.0**-132
+    # e4m3 smallest subnormal is 2^-9
+    assert nx.to_e4m3_sat(2.0**-10) == 0.0
+    assert nx.to_e4m3_sat(3 * 2.0**-10) == 2.0**-8
