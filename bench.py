@@ -1,0 +1,268 @@
+"""Bench of the single-GPU expert-parallel MoE layer on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path -- route, layout, dispatch, gate/up
+GEMM + SwiGLU, down GEMM, combine -- over one batch of seeded synthetic
+input already resident in HBM.  The default workload is the DeepSeek-V3
+shaped decode step (T=128, E=256, K=8, H=7168, I=2048, bf16).  Each stage
+is bracketed by HIP events on the launch stream during the timed steps, so
+per-kernel durations, algorithmic GB/s and TFLOP/s come from the same run.
+
+Prints one JSON line (rank 0).  A CPU baseline -- the oracle as it stands,
+timed on a bounded sample of the same workload on the host cores -- is
+included unless --no-cpu-baseline is given.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+ESIZE = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_decode", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0,
+                    help="target CPU seconds for the oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work per stage (what the method must move / compute)
+# ----------------------------------------------------------------------------
+def stage_work(cfg, counts_local, tokens_with_local):
+    T, E, K, H, I = cfg.T, cfg.E, cfg.K, cfg.H, cfg.I
+    R = int(counts_local.sum())
+    touched = int((counts_local > 0).sum())
+    sx, sa, sw, sy, so = (ESIZE[cfg.x_dtype], ESIZE[cfg.act_dtype], ESIZE[cfg.w_dtype],
+                          ESIZE[cfg.y_dtype], ESIZE[cfg.out_dtype])
+    nbH, nbI = -(-H // 128), -(-I // 128)
+    fp8 = cfg.act_dtype == "fp8"
+    sc_x = R * nbH * 4 if fp8 else 0
+    sc_h = R * nbI * 4 if fp8 else 0
+    sc_wgu = touched * 2 * I * nbH * 4 if cfg.w_dtype == "fp8" else 0
+    sc_wd = touched * H * nbI * 4 if cfg.w_dtype == "fp8" else 0
+    w = {
+        "route": dict(bytes=T * E * 4 + T * K * 8, flops=0),
+        "layout": dict(bytes=T * K * 4 * 3 + cfg.cap * 4 + E * 4 * 2, flops=0),
+        "dispatch": dict(bytes=tokens_with_local * H * sx + R * H * sa + sc_x, flops=0),
+        "ffn_gate_up": dict(bytes=touched * 2 * I * H * sw + sc_wgu + R * H * sa + sc_x
+                            + R * I * sa + sc_h, flops=4 * R * H * I),
+        "ffn_down": dict(bytes=touched * H * I * sw + sc_wd + R * I * sa + sc_h + R * H * sy,
+                         flops=2 * R * H * I),
+        "combine": dict(bytes=R * H * sy + T * H * so + T * K * 8, flops=0),
+    }
+    return w, R, touched
+
+
+def roofline_of(work, ms, mfma_peak):
+    t = ms / 1e3
+    gbs = work["bytes"] / t / 1e9
+    tfl = work["flops"] / t / 1e12
+    hbm_floor = work["bytes"] / (HBM_PEAK_GBS * 1e9)
+    mfma_floor = work["flops"] / (mfma_peak * 1e12) if work["flops"] else 0.0
+    if mfma_floor > hbm_floor:
+        return {"bound": "mfma", "achieved": round(tfl, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(tfl / mfma_peak, 4)}
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ----------------------------------------------------------------------------
+def cpu_baseline(cfg, x_cpu, logits_cpu, weights, budget_s):
+    import oracle
+    from oracle import numerics as nx
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+
+    def wnp(j):
+        d = weights.expert(j, "cpu")
+        if cfg.w_dtype == "fp8":
+            return tuple(nx.dequantize_fp8_blocks(d[k].float().numpy().astype(np.float64),
+                                                  d[k + "_scale"].numpy()) for k in ("gate", "up", "down"))
+        return tuple(d[k].float().numpy().astype(np.float64) for k in ("gate", "up", "down"))
+
+    x = np.concatenate([s.float().numpy().astype(np.float64) for s in x_cpu])
+    lg = logits_cpu.numpy()
+    t0 = time.perf_counter()
+    ids, gates = oracle.route(lg, cfg.K)
+    lay = oracle.layout(ids, cfg.E, cfg.e_begin, cfg.e_end, cfg.cap)
+    t_route_layout = time.perf_counter() - t0
+    R = int(lay["offsets"][-1])
+    off = lay["offsets"]
+    touched = [j for j in range(cfg.E_loc) if off[j + 1] > off[j]]
+    # dispatch + FFN + combine over a growing prefix of the touched experts
+    done, t_ffn, rows_done = 0, 0.0, 0
+    t_disp = 0.0
+    for j in touched:
+        a, b = int(off[j]), int(off[j + 1])
+        W = wnp(j)                                      # weight fetch: not timed
+        t1 = time.perf_counter()
+        xd, xs = oracle.dispatch(x[lay["src_of"][a:b] // cfg.K], np.arange(b - a)[:, None], b - a,
+                                 cfg.act_dtype)
+        t2 = time.perf_counter()
+        xv = nx.dequantize_fp8_blocks(xd, xs) if cfg.act_dtype == "fp8" else xd
+        oracle.expert_ffn(xv, *W, cfg.act_dtype, cfg.y_dtype)
+        t3 = time.perf_counter()
+        t_disp += t2 - t1
+        t_ffn += t3 - t2
+        done += 1
+        rows_done += b - a
+        if t_route_layout + t_disp + t_ffn > budget_s:
+            break
+    scale = len(touched) / max(done, 1)
+    # combine over all tokens with synthetic y of the right shape (cost is shape-bound)
+    y = np.zeros((R, cfg.H))
+    t4 = time.perf_counter()
+    oracle.combine(y, lay["row_of"], gates, cfg.out_dtype)
+    t_comb = time.perf_counter() - t4
+    est = t_route_layout + (t_disp + t_ffn) * scale + t_comb
+    return {"value": round(cfg.T / est, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"route+layout+combine on all {cfg.T} tokens; dispatch+FFN on {done} of "
+                       f"{len(touched)} touched experts ({rows_done} of {R} rows), scaled by "
+                       f"{scale:.2f}; weight fetch to host untimed"),
+            "measured_s": round(t_route_layout + t_disp + t_ffn + t_comb, 2)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    import combine_grouped_gemm_amd as m
+    m.lib()                                     # loud failure if the HIP library is missing
+    cfg = wl.CONFIGS[a.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    x_cpu = wl.gen_x(cfg)
+    logits_cpu = wl.gen_logits(cfg, x_cpu)
+    x = [s.to(dev) for s in x_cpu]
+    logits = logits_cpu.to(dev)
+    W = wl.gen_expert_weights(cfg, device=dev)
+    wdict = {"gate": W.gate, "up": W.up, "down": W.down}
+    if cfg.w_dtype == "fp8":
+        wdict.update(gate_scale=W.gate_scale, up_scale=W.up_scale, down_scale=W.down_scale)
+    layer = m.MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end,
+                       cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=dev)
+    stages = layer.stages(x, logits, wdict)
+
+    # parity gate before timing: routing and layout must equal the oracle's
+    layer.forward(x, logits, wdict)
+    torch.cuda.synchronize()
+    import oracle
+    ids, _ = oracle.route(logits_cpu.numpy(), cfg.K)
+    lay = oracle.layout(ids, cfg.E, cfg.e_begin, cfg.e_end, cfg.cap)
+    if not (np.array_equal(layer.topk_ids.cpu().numpy(), ids)
+            and np.array_equal(layer.row_of.cpu().numpy(), lay["row_of"])):
+        print(json.dumps({"error": "parity gate failed: routing/layout differ from the oracle"}))
+        sys.exit(1)
+    counts_local = lay["counts"][cfg.e_begin:cfg.e_end]
+    local = (ids >= cfg.e_begin) & (ids < cfg.e_end)
+    work, R, touched = stage_work(cfg, counts_local, int(local.any(axis=1).sum()))
+
+    stream = torch.cuda.current_stream()
+    for _ in range(a.warmup):
+        for _, run in stages:
+            run()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({a.warmup} steps), timing {a.steps}", file=sys.stderr, flush=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        ev[s][0].record(stream)
+        for i, (_, run) in enumerate(stages):
+            run()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: [] for name, _ in stages}
+    step_ms = []
+    for s in range(a.steps):
+        for i, (name, _) in enumerate(stages):
+            per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
+        step_ms.append(ev[s][0].elapsed_time(ev[s][-1]))
+    ms_per_step = wall * 1e3 / a.steps
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.act_dtype]
+    stage_rep = {}
+    for name, _ in stages:
+        ms = float(np.mean(per[name]))
+        r = roofline_of(work[name], ms, mfma_peak)
+        stage_rep[name] = {"ms": round(ms, 4), "ms_p10": round(float(np.percentile(per[name], 10)), 4),
+                           "ms_p90": round(float(np.percentile(per[name], 90)), 4),
+                           "GB_s": round(work[name]["bytes"] / (ms / 1e3) / 1e9, 1),
+                           "TFLOP_s": round(work[name]["flops"] / (ms / 1e3) / 1e12, 2),
+                           "hbm_frac": round(work[name]["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "mfma_frac": round(work[name]["flops"] / (ms / 1e3) / 1e12 / mfma_peak, 4),
+                           "bytes": int(work[name]["bytes"]), "flops": int(work[name]["flops"]),
+                           "bound": r["bound"]}
+    dom = max(stage_rep, key=lambda k: stage_rep[k]["ms"])
+    roof = roofline_of(work[dom], stage_rep[dom]["ms"], mfma_peak)
+    roof.update({"kernel": dom, "traffic": None})
+    ffn_ms = stage_rep["ffn_gate_up"]["ms"] + stage_rep["ffn_down"]["ms"]
+    ffn_flops = work["ffn_gate_up"]["flops"] + work["ffn_down"]["flops"]
+    ffn_bytes = work["ffn_gate_up"]["bytes"] + work["ffn_down"]["bytes"]
+    res = {
+        "metric": "MoE-layer tokens/s on 1 GPU",
+        "value": round(cfg.T / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_events": round(float(np.mean(step_ms)), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.act_dtype, "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "K": cfg.K, "H": cfg.H, "I": cfg.I,
+                   "local_experts": [cfg.e_begin, cfg.e_end], "segments": len(cfg.seg_rows),
+                   "rows": R, "experts_touched": touched},
+        "roofline": roof,
+        "grouped_ffn": {"ms": round(ffn_ms, 4), "TFLOP_s": round(ffn_flops / (ffn_ms / 1e3) / 1e12, 2),
+                        "mfma_frac": round(ffn_flops / (ffn_ms / 1e3) / 1e12 / mfma_peak, 4),
+                        "GB_s": round(ffn_bytes / (ffn_ms / 1e3) / 1e9, 1),
+                        "hbm_frac": round(ffn_bytes / (ffn_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "stages": stage_rep,
+    }
+    if a.copy_calibration_mib:
+        n = a.copy_calibration_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, x_cpu, logits_cpu, W, a.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,292 @@
+"""Python binding of libmoeep: the single-GPU expert-parallel MoE layer path
+(route -> layout -> dispatch -> grouped SwiGLU FFN -> combine) on MI355X.
+
+Each function here has the name of the C entry point it marshals (see
+include/moeep.h for the full contract).  Tensors are torch device tensors
+used only as memory; the binding checks shapes and dtypes, allocates outputs
+the caller did not provide, passes ``data_ptr()`` and the current HIP stream,
+and raises :class:`MoeError` with the library's message on a non-OK status.
+All compute happens in the HIP kernels of ``libmoeep.so``; there is no other
+code path.  Build the library with ``python -m combine_grouped_gemm_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["MoeError", "lib", "library_path", "moe_version", "moe_route",
+           "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
+           "moe_ffn_workspace_bytes", "moe_ffn_gate_up", "moe_ffn_down",
+           "moe_grouped_ffn", "moe_combine", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
+           "MoELayer"]
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+FP8_BLOCK = 128
+MAX_SEGMENTS = 64
+
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
+_TORCH = {v: k for k, v in _DT.items()}
+_NAMES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeep.so")
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+def _status_name(s):
+    return {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
+            3: "MOE_ERR_HIP"}.get(s, f"status {s}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoeep.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"libmoeep.so is missing at {library_path}; build it with "
+                           "'python -m combine_grouped_gemm_amd.build'")
+    L = ctypes.CDLL(library_path)
+    P, I, Z, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "moe_status_string": ([I], ctypes.c_char_p),
+        "moe_last_error": ([], ctypes.c_char_p),
+        "moe_version": ([], ctypes.c_char_p),
+        "moe_route": ([P, I, I, I, P, P, P], S),
+        "moe_layout_workspace_bytes": ([I, I, I], Z),
+        "moe_layout": ([P, I, I, I, I, I, P, P, P, P, I, P, Z, P], S),
+        "moe_dispatch": ([P, P, I, I, I, P, I, P, I, P, I, P], S),
+        "moe_ffn_workspace_bytes": ([I, I, I], Z),
+        "moe_ffn_gate_up": ([P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, P], S),
+        "moe_ffn_down": ([P, P, P, I, I, I, I, I, P, P, I, P, I, P], S),
+        "moe_grouped_ffn": ([P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, I, P, Z, P], S),
+        "moe_combine": ([P, I, I, P, P, I, I, I, P, I, P], S),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes, f.restype = args, res
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
+    return t
+
+
+def _dtype_code(d):
+    if isinstance(d, str):
+        return _NAMES[d]
+    if isinstance(d, torch.dtype):
+        return _DT[d]
+    return int(d)
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()
+
+
+# ----------------------------------------------------------------------------
+def moe_route(logits, K: int, topk_ids=None, topk_w=None, stream=None):
+    """Top-K expert ids (B, K) int32 and renormalised softmax gates (B, K) fp32."""
+    _dev(logits, "logits", torch.float32, 2)
+    B, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((B, K), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((B, K), dtype=torch.float32, device=logits.device)
+    _dev(topk_ids, "topk_ids", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32)
+    _check(lib().moe_route(_ptr(logits), B, E, K, _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_layout_workspace_bytes(B: int, K: int, E: int) -> int:
+    return int(lib().moe_layout_workspace_bytes(B, K, E))
+
+
+def moe_layout(topk_ids, E: int, e_begin: int, e_end: int, cap_rows: int, counts=None,
+               offsets=None, row_of=None, src_of=None, ws=None, stream=None) -> dict:
+    """counts (E), offsets (E_loc+1), row_of (B, K), src_of (cap_rows), all int32."""
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    B, K = topk_ids.shape
+    dev = topk_ids.device
+    E_loc = e_end - e_begin
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(max(E_loc, 0) + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_of = torch.empty((B, K), dtype=torch.int32, device=dev) if row_of is None else row_of
+    src_of = torch.empty(max(cap_rows, 1), dtype=torch.int32, device=dev) if src_of is None else src_of
+    need = moe_layout_workspace_bytes(B, K, E)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    for n, t in (("counts", counts), ("offsets", offsets), ("row_of", row_of), ("src_of", src_of)):
+        _dev(t, n, torch.int32)
+    _dev(ws, "ws")
+    _check(lib().moe_layout(_ptr(topk_ids), B, K, E, e_begin, e_end, _ptr(counts), _ptr(offsets),
+                            _ptr(row_of), _ptr(src_of), cap_rows, _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)))
+    return {"counts": counts, "offsets": offsets, "row_of": row_of, "src_of": src_of}
+
+
+def moe_dispatch(seg_x, row_of, cap_rows: int, xd_dtype=None, xd=None, xd_scales=None,
+                 stream=None):
+    """Scatter the token rows of the segments into xd (cap_rows, H); fp8
+    storage also fills xd_scales (cap_rows, ceil(H/128))."""
+    if isinstance(seg_x, torch.Tensor):
+        seg_x = [seg_x]
+    seg_x = list(seg_x)
+    if not 1 <= len(seg_x) <= MAX_SEGMENTS:
+        raise ValueError(f"need 1..{MAX_SEGMENTS} segments")
+    x_dt = seg_x[0].dtype
+    H = seg_x[0].shape[1]
+    for i, s in enumerate(seg_x):
+        _dev(s, f"seg_x[{i}]", x_dt, 2)
+        if s.shape[1] != H:
+            raise ValueError("all segments need the same H")
+    _dev(row_of, "row_of", torch.int32, 2)
+    K = row_of.shape[1]
+    dev = row_of.device
+    xd_code = _DT[x_dt] if xd_dtype is None else _dtype_code(xd_dtype)
+    if xd is None:
+        xd = torch.empty((max(cap_rows, 1), H), dtype=_TORCH[xd_code], device=dev)
+    if xd_code == MOE_FP8_E4M3 and xd_scales is None:
+        xd_scales = torch.empty((max(cap_rows, 1), -(-H // FP8_BLOCK)), dtype=torch.float32, device=dev)
+    _dev(xd, "xd")
+    ptrs = (ctypes.c_void_p * len(seg_x))(*[s.data_ptr() for s in seg_x])
+    rows = (ctypes.c_int32 * len(seg_x))(*[s.shape[0] for s in seg_x])
+    _check(lib().moe_dispatch(ctypes.cast(ptrs, ctypes.c_void_p), ctypes.cast(rows, ctypes.c_void_p),
+                              len(seg_x), _DT[x_dt], H, _ptr(row_of), K, _ptr(xd), xd_code,
+                              _ptr(xd_scales), cap_rows, _stream(stream)))
+    return xd, xd_scales
+
+
+def moe_ffn_workspace_bytes(cap_rows: int, I: int, act_dtype) -> int:
+    return int(lib().moe_ffn_workspace_bytes(cap_rows, I, _dtype_code(act_dtype)))
+
+
+def _ffn_shapes(a, w_gate_or_down, gated):
+    E_loc = w_gate_or_down.shape[0]
+    if gated:
+        I, H = w_gate_or_down.shape[1], w_gate_or_down.shape[2]
+    else:
+        H, I = w_gate_or_down.shape[1], w_gate_or_down.shape[2]
+    return E_loc, H, I
+
+
+def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_up_scales=None,
+                    h=None, h_scales=None, stream=None):
+    """h = silu(Xd Wg^T) * (Xd Wu^T) per local expert -> (cap_rows, I) [+ scales]."""
+    _dev(xd, "xd", ndim=2)
+    _dev(offsets, "offsets", torch.int32, 1)
+    _dev(w_gate, "w_gate", xd.dtype, 3)
+    _dev(w_up, "w_up", xd.dtype, 3)
+    E_loc, H, I = _ffn_shapes(xd, w_gate, True)
+    cap = xd.shape[0]
+    act = _DT[xd.dtype]
+    if h is None:
+        h = torch.empty((cap, I), dtype=xd.dtype, device=xd.device)
+    if act == MOE_FP8_E4M3 and h_scales is None:
+        h_scales = torch.empty((cap, -(-I // FP8_BLOCK)), dtype=torch.float32, device=xd.device)
+    _check(lib().moe_ffn_gate_up(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, cap, H, I, act,
+                                 _ptr(w_gate), _ptr(w_up), _ptr(w_gate_scales), _ptr(w_up_scales),
+                                 act, _ptr(h), _ptr(h_scales), _stream(stream)))
+    return h, h_scales
+
+
+def _y_dtype_for(act):
+    return torch.float32 if act == MOE_F32 else torch.bfloat16
+
+
+def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dtype=None,
+                 stream=None):
+    """y = h Wd^T per local expert -> (cap_rows, H)."""
+    _dev(h, "h", ndim=2)
+    _dev(offsets, "offsets", torch.int32, 1)
+    _dev(w_down, "w_down", h.dtype, 3)
+    E_loc, H, I = _ffn_shapes(h, w_down, False)
+    cap = h.shape[0]
+    act = _DT[h.dtype]
+    y_dtype = _y_dtype_for(act) if y_dtype is None else y_dtype
+    if y is None:
+        y = torch.empty((cap, H), dtype=y_dtype, device=h.device)
+    _check(lib().moe_ffn_down(_ptr(h), _ptr(h_scales), _ptr(offsets), E_loc, cap, H, I, act,
+                              _ptr(w_down), _ptr(w_down_scales), act, _ptr(y), _DT[y.dtype],
+                              _stream(stream)))
+    return y
+
+
+def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=None,
+                    w_up_scales=None, w_down_scales=None, y=None, y_dtype=None, ws=None,
+                    stream=None):
+    """Both FFN stages with h held in the workspace ``ws``."""
+    _dev(xd, "xd", ndim=2)
+    _dev(offsets, "offsets", torch.int32, 1)
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _dev(w, n, xd.dtype, 3)
+    E_loc, H, I = _ffn_shapes(xd, w_gate, True)
+    cap = xd.shape[0]
+    act = _DT[xd.dtype]
+    y_dtype = _y_dtype_for(act) if y_dtype is None else y_dtype
+    if y is None:
+        y = torch.empty((cap, H), dtype=y_dtype, device=xd.device)
+    need = moe_ffn_workspace_bytes(cap, I, act)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=xd.device)
+    _check(lib().moe_grouped_ffn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, cap, H, I, act,
+                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
+                                 _ptr(w_up_scales), _ptr(w_down_scales), act, _ptr(y),
+                                 _DT[y.dtype], _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)))
+    return y
+
+
+def moe_combine(y, row_of, topk_w, out=None, out_dtype=None, stream=None):
+    """out[t] = sum_k topk_w[t,k] * y[row_of[t,k]] over local slots -> (B, H)."""
+    _dev(y, "y", ndim=2)
+    _dev(row_of, "row_of", torch.int32, 2)
+    _dev(topk_w, "topk_w", torch.float32, 2)
+    B, K = row_of.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((B, H), dtype=y.dtype if out_dtype is None else out_dtype, device=y.device)
+    _dev(out, "out")
+    _check(lib().moe_combine(_ptr(y), _DT[y.dtype], y.shape[0], _ptr(row_of), _ptr(topk_w), B, K, H,
+                             _ptr(out), _DT[out.dtype], _stream(stream)))
+    return out
+
+
+from .layer import MoELayer  # noqa: E402  (uses the functions above)

@@ -1,0 +1,290 @@
+// C ABI of libmoeep: host-side argument checks, then kernel launches on the
+// caller's stream.  Nothing here allocates, synchronises or copies from the
+// device; a failed check returns before anything is enqueued.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+#include "moeep.h"
+
+namespace moeep {
+
+int device_cu_count() {
+    static thread_local int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
+}
+
+}  // namespace moeep
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+moe_status_t launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                        \
+    do {                                                          \
+        if (!(cond)) return fail(MOE_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+moe_status_t check_route_shape(int B, int E, int K) {
+    REQUIRE(B >= 0, "B must be >= 0 (got %d)", B);
+    REQUIRE(E >= 1 && E <= 1024, "E must be in [1, 1024] (got %d)", E);
+    REQUIRE(K >= 1 && K <= E, "K must be in [1, E] (got K=%d, E=%d)", K, E);
+    REQUIRE((long long)B * K <= 0x7fffffffLL && (long long)B * E <= 0x7fffffffLL,
+            "B*K and B*E must fit in int32");
+    return MOE_OK;
+}
+
+moe_status_t check_ffn_common(const void* a, const int32_t* offsets, int E_local, int cap_rows,
+                              int H, int I, moe_dtype_t act_dt, moe_dtype_t w_dt) {
+    REQUIRE(a && offsets, "null activation or offsets pointer");
+    REQUIRE(E_local >= 1 && E_local <= 1024, "E_local must be in [1, 1024] (got %d)", E_local);
+    REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
+    REQUIRE(H >= 64 && H % 64 == 0 && I >= 64 && I % 64 == 0,
+            "H and I must be positive multiples of 64 (got H=%d, I=%d)", H, I);
+    REQUIRE((long long)cap_rows * (H > I ? H : I) <= 0x7fffffffLL * 4LL, "cap_rows * H too large");
+    REQUIRE(aligned16(a), "activation pointer must be 16-byte aligned");
+    const bool ok = (act_dt == MOE_F32 && w_dt == MOE_F32) || (act_dt == MOE_BF16 && w_dt == MOE_BF16) ||
+                    (act_dt == MOE_FP8_E4M3 && w_dt == MOE_FP8_E4M3);
+    if (!ok) return fail(MOE_ERR_UNSUPPORTED, "unsupported (act_dt, w_dt) = (%d, %d)", act_dt, w_dt);
+    return MOE_OK;
+}
+
+moe_status_t check_y_dtype(moe_dtype_t act_dt, moe_dtype_t y_dt) {
+    const bool ok = (act_dt == MOE_F32 && y_dt == MOE_F32) || (act_dt == MOE_BF16 && y_dt == MOE_BF16) ||
+                    (act_dt == MOE_FP8_E4M3 && y_dt == MOE_BF16);
+    if (!ok) return fail(MOE_ERR_UNSUPPORTED, "unsupported (act_dt, y_dt) = (%d, %d)", act_dt, y_dt);
+    return MOE_OK;
+}
+
+moeep::FfnArgs ffn_args(const void* a, const float* a_scales, const int32_t* offsets, int E_local,
+                        int cap_rows, int Kdim, int N, const void* w0, const void* w1,
+                        const float* w0s, const float* w1s, void* out, float* out_scales) {
+    moeep::FfnArgs f;
+    f.a = a;
+    f.a_scales = a_scales;
+    f.offsets = offsets;
+    f.E_loc = E_local;
+    f.cap = cap_rows;
+    f.Kdim = Kdim;
+    f.N = N;
+    f.w0 = w0;
+    f.w1 = w1;
+    f.w0_scales = w0s;
+    f.w1_scales = w1s;
+    f.out = out;
+    f.out_scales = out_scales;
+    f.rows_hint = cap_rows / E_local;
+    return f;
+}
+
+hipError_t run_ffn(const moeep::FfnArgs& f, moe_dtype_t act_dt, bool gated, hipStream_t stream) {
+    if (f.cap == 0) return hipSuccess;
+    switch (act_dt) {
+        case MOE_F32: return moeep::launch_ffn_f32(f, gated, stream);
+        case MOE_BF16: return moeep::launch_ffn_bf16(f, gated, stream);
+        default: return moeep::launch_ffn_fp8(f, gated, stream);
+    }
+}
+
+size_t elem_size(moe_dtype_t d) { return d == MOE_F32 ? 4 : d == MOE_BF16 ? 2 : 1; }
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+const char* moe_version(void) { return "libmoeep 0.1 (gfx950)"; }
+
+moe_status_t moe_route(const float* logits, int B, int E, int K, int32_t* topk_ids, float* topk_w,
+                       hipStream_t stream) {
+    moe_status_t s = check_route_shape(B, E, K);
+    if (s != MOE_OK) return s;
+    if (B > 0) REQUIRE(logits && topk_ids && topk_w, "null pointer argument");
+    return launched(moeep::launch_route(logits, B, E, K, topk_ids, topk_w, stream), "moe_route");
+}
+
+size_t moe_layout_workspace_bytes(int B, int K, int E) {
+    if (B < 0 || K < 1 || E < 1) return 0;
+    return moeep::layout_workspace_bytes(B, K, E);
+}
+
+moe_status_t moe_layout(const int32_t* topk_ids, int B, int K, int E, int e_begin, int e_end,
+                        int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                        int cap_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+    moe_status_t s = check_route_shape(B, E, K);
+    if (s != MOE_OK) return s;
+    REQUIRE(e_begin >= 0 && e_begin < e_end && e_end <= E,
+            "need 0 <= e_begin < e_end <= E (got %d, %d, E=%d)", e_begin, e_end, E);
+    REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
+    REQUIRE(counts && offsets && ws, "null counts, offsets or workspace");
+    if (B > 0) REQUIRE(topk_ids && row_of, "null topk_ids or row_of");
+    if (cap_rows > 0) REQUIRE(src_of, "null src_of");
+    REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, "workspace must be 256-byte aligned");
+    REQUIRE(ws_bytes >= moeep::layout_workspace_bytes(B, K, E),
+            "workspace too small: %zu < %zu bytes", ws_bytes, moeep::layout_workspace_bytes(B, K, E));
+    return launched(moeep::launch_layout(topk_ids, B, K, E, e_begin, e_end, counts, offsets, row_of,
+                                         src_of, cap_rows, ws, stream),
+                    "moe_layout");
+}
+
+moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int n_seg,
+                          moe_dtype_t x_dt, int H, const int32_t* row_of, int K, void* xd,
+                          moe_dtype_t xd_dt, float* xd_scales, int cap_rows, hipStream_t stream) {
+    REQUIRE(n_seg >= 1 && n_seg <= MOE_MAX_SEGMENTS, "n_seg must be in [1, %d]", MOE_MAX_SEGMENTS);
+    REQUIRE(seg_x && seg_rows, "null segment tables");
+    REQUIRE(K >= 1 && K <= 1024, "K must be in [1, 1024]");
+    REQUIRE(H >= 64 && H % 64 == 0, "H must be a positive multiple of 64 (got %d)", H);
+    REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
+    int kind;
+    if (x_dt == MOE_F32 && xd_dt == MOE_F32) kind = 0;
+    else if (x_dt == MOE_BF16 && xd_dt == MOE_BF16) kind = 1;
+    else if (x_dt == MOE_BF16 && xd_dt == MOE_FP8_E4M3) kind = 2;
+    else return fail(MOE_ERR_UNSUPPORTED, "unsupported dispatch (x_dt, xd_dt) = (%d, %d)", x_dt, xd_dt);
+    moeep::SegTable seg;
+    seg.n = n_seg;
+    seg.start[0] = 0;
+    long long B = 0;
+    for (int i = 0; i < n_seg; ++i) {
+        REQUIRE(seg_rows[i] >= 0, "seg_rows[%d] < 0", i);
+        if (seg_rows[i] > 0) {
+            REQUIRE(seg_x[i] != nullptr, "seg_x[%d] is null", i);
+            REQUIRE(aligned16(seg_x[i]), "seg_x[%d] must be 16-byte aligned", i);
+        }
+        seg.ptr[i] = seg_x[i];
+        B += seg_rows[i];
+        REQUIRE(B * K <= 0x7fffffffLL, "total tokens * K must fit in int32");
+        seg.start[i + 1] = (int)B;
+    }
+    if (B > 0) {
+        REQUIRE(row_of && xd, "null row_of or xd");
+        REQUIRE(aligned16(xd), "xd must be 16-byte aligned");
+        if (kind == 2) REQUIRE(xd_scales, "fp8 dispatch needs xd_scales");
+    }
+    return launched(moeep::launch_dispatch(seg, (int)B, H, kind, row_of, K, xd, xd_scales, cap_rows, stream),
+                    "moe_dispatch");
+}
+
+size_t moe_ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt) {
+    if (cap_rows < 0 || I < 1) return 0;
+    size_t bytes = round256((size_t)cap_rows * I * elem_size(act_dt));
+    if (act_dt == MOE_FP8_E4M3) bytes += round256((size_t)cap_rows * ((I + 127) / 128) * sizeof(float));
+    return bytes;
+}
+
+moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32_t* offsets,
+                             int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
+                             const void* w_gate, const void* w_up, const float* w_gate_scales,
+                             const float* w_up_scales, moe_dtype_t w_dt, void* h, float* h_scales,
+                             hipStream_t stream) {
+    moe_status_t s = check_ffn_common(xd, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
+    if (s != MOE_OK) return s;
+    REQUIRE(w_gate && w_up && h, "null weight or h pointer");
+    REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(h), "weights and h must be 16-byte aligned");
+    if (act_dt == MOE_FP8_E4M3)
+        REQUIRE(xd_scales && w_gate_scales && w_up_scales && h_scales, "fp8 needs all scale pointers");
+    auto f = ffn_args(xd, xd_scales, offsets, E_local, cap_rows, H, I, w_gate, w_up, w_gate_scales,
+                      w_up_scales, h, h_scales);
+    return launched(run_ffn(f, act_dt, true, stream), "moe_ffn_gate_up");
+}
+
+moe_status_t moe_ffn_down(const void* h, const float* h_scales, const int32_t* offsets, int E_local,
+                          int cap_rows, int H, int I, moe_dtype_t act_dt, const void* w_down,
+                          const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
+                          hipStream_t stream) {
+    moe_status_t s = check_ffn_common(h, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
+    if (s != MOE_OK) return s;
+    s = check_y_dtype(act_dt, y_dt);
+    if (s != MOE_OK) return s;
+    REQUIRE(w_down && y, "null weight or y pointer");
+    REQUIRE(aligned16(w_down) && aligned16(y), "weights and y must be 16-byte aligned");
+    if (act_dt == MOE_FP8_E4M3) REQUIRE(h_scales && w_down_scales, "fp8 needs all scale pointers");
+    auto f = ffn_args(h, h_scales, offsets, E_local, cap_rows, I, H, w_down, nullptr, w_down_scales,
+                      nullptr, y, nullptr);
+    return launched(run_ffn(f, act_dt, false, stream), "moe_ffn_down");
+}
+
+moe_status_t moe_grouped_ffn(const void* xd, const float* xd_scales, const int32_t* offsets,
+                             int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const float* w_gate_scales, const float* w_up_scales,
+                             const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+    moe_status_t s = check_ffn_common(xd, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
+    if (s != MOE_OK) return s;
+    s = check_y_dtype(act_dt, y_dt);
+    if (s != MOE_OK) return s;
+    REQUIRE(ws, "null workspace");
+    REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, "workspace must be 256-byte aligned");
+    const size_t need = moe_ffn_workspace_bytes(cap_rows, I, act_dt);
+    REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    void* h = ws;
+    float* h_scales = nullptr;
+    if (act_dt == MOE_FP8_E4M3)
+        h_scales = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)cap_rows * I));
+    s = moe_ffn_gate_up(xd, xd_scales, offsets, E_local, cap_rows, H, I, act_dt, w_gate, w_up,
+                        w_gate_scales, w_up_scales, w_dt, h, h_scales, stream);
+    if (s != MOE_OK) return s;
+    return moe_ffn_down(h, h_scales, offsets, E_local, cap_rows, H, I, act_dt, w_down, w_down_scales,
+                        w_dt, y, y_dt, stream);
+}
+
+moe_status_t moe_combine(const void* y, moe_dtype_t y_dt, int cap_rows, const int32_t* row_of,
+                         const float* topk_w, int B, int K, int H, void* out, moe_dtype_t out_dt,
+                         hipStream_t stream) {
+    REQUIRE(B >= 0 && K >= 1 && K <= 1024, "need B >= 0 and 1 <= K <= 1024");
+    REQUIRE((long long)B * K <= 0x7fffffffLL, "B*K must fit in int32");
+    REQUIRE(H >= 64 && H % 64 == 0, "H must be a positive multiple of 64 (got %d)", H);
+    REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
+    int kind;
+    if (y_dt == MOE_F32 && out_dt == MOE_F32) kind = 0;
+    else if (y_dt == MOE_BF16 && out_dt == MOE_BF16) kind = 1;
+    else if (y_dt == MOE_BF16 && out_dt == MOE_F32) kind = 2;
+    else return fail(MOE_ERR_UNSUPPORTED, "unsupported combine (y_dt, out_dt) = (%d, %d)", y_dt, out_dt);
+    if (B > 0) {
+        REQUIRE(y && row_of && topk_w && out, "null pointer argument");
+        REQUIRE(aligned16(y) && aligned16(out), "y and out must be 16-byte aligned");
+    }
+    return launched(moeep::launch_combine(y, kind, row_of, topk_w, B, K, H, out, cap_rows, stream),
+                    "moe_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Device helpers shared by the libmoeep kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moeep {
+
+constexpr int kWave = 64;
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest even; NaN stays NaN, overflow becomes inf.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// OCP fp8 e4m3fn: encode with round-to-nearest-even after saturating the
+// magnitude to 448 (the largest finite code).  Subnormal quantum is 2^-9.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
+    uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    float a = fabsf(v);
+    if (!(a <= 448.0f)) a = 448.0f;
+    uint32_t au = __float_as_uint(a);
+    if (au < 0x3c800000u) {                       // a < 2^-6: subnormal codes 0..8
+        return sign | (uint32_t)rintf(a * 512.0f);
+    }
+    uint32_t r = (au + 0x7ffffu + ((au >> 20) & 1u)) >> 20;   // keep 3 fraction bits
+    return sign | (r - (120u << 3));              // rebias exponent 127 -> 7
+}
+
+// ---------------------------------------------------------------------------
+// wave helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Mask of the lanes whose `key` equals this lane's, among lanes in `active`.
+// `nbits` bits of the key are compared (keys must be < 2^nbits).
+__device__ __forceinline__ uint64_t match_mask(uint32_t key, uint64_t active, int nbits) {
+    uint64_t m = active;
+    for (int b = 0; b < nbits; ++b) {
+        bool bit = (key >> b) & 1u;
+        uint64_t bal = ballot64(bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace moeep

@@ -1,0 +1,300 @@
+// Grouped SwiGLU expert FFN with fp8 e4m3 operands and fp32 1x128 block
+// scales (SGLang "Expert Parallelism", MoE-runner backend table: block-wise
+// fp8 quantisation for the grouped GEMM; the block geometry is this
+// library's convention, one scale per 128 contraction elements).
+//
+// Same ragged persistent tile walk as the bf16 kernel.  One k-step is one
+// 128-wide scale block: v_mfma_f32_16x16x128_f8f6f4 (both operands OCP
+// e4m3) produces the unscaled block product from a zero accumulator, which
+// is folded into the fp32 accumulator as acc += partial * sa[row] * sb[col].
+// Lane l feeds row (l % 16) with bytes [32*(l/16), 32*(l/16)+32) of the
+// block for both operands.  A 64-wide tail block (K = 2880) is zero-filled
+// on both operands.
+//
+// gate/up writes h as fp8: each tile covers exactly one 128-column block of
+// h per row, so the block amax is reduced inside the tile (16 lanes by xor
+// shuffles, then the waves of a row through LDS), s = amax / 448 and the
+// codes are written with the scale.
+#include "grouped_tiles.hpp"
+
+namespace moeep {
+namespace {
+
+constexpr int BKB = 128;          // bytes (= fp8 elements) per k-step
+
+template <int BM, int BN, int WMW, int WNW, bool GATED>
+__global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArgs p) {
+    constexpr int NT = 64 * WMW * WNW;
+    constexpr int FM = BM / 16 / WMW;
+    constexpr int WN = BN / WNW;
+    constexpr int FN = WN / 16;
+    constexpr int BNO = GATED ? BN / 2 : BN;
+    static_assert(FM >= 1 && FN >= 1 && (!GATED || (FN % 2 == 0 && BNO == 128)), "tile shape");
+    static_assert(BM + BN <= NT, "scale loads use disjoint thread ranges");
+    constexpr int A_IT = (BM * 8 + NT - 1) / NT;
+    constexpr int B_IT = (BN * 8 + NT - 1) / NT;
+
+    __shared__ uint4 sA[BM * 8];
+    __shared__ uint4 sB[BN * 8];
+    __shared__ float sAs[BM];
+    __shared__ float sBs[BN];
+    __shared__ float s_amax[WNW][BM];
+    __shared__ int s_pre[kMaxExperts + 1];
+    __shared__ int s_tmp[NT / kWave];
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / WNW, wn = wave % WNW;
+    const int Kdim = p.Kdim, N = p.N, cap = p.cap;
+    const int nbK = (Kdim + BKB - 1) / BKB;
+    const int nbN = (N + 127) / 128;
+
+    build_tile_prefix<NT, BM>(p.offsets, p.E_loc, cap, s_pre, s_tmp);
+    const int n_tiles_n = (N + BNO - 1) / BNO;
+    const int total = n_tiles_n * s_pre[p.E_loc];
+    const int G = gridDim.x;
+    const int v = xcd_block_order();
+
+    const uint8_t* __restrict__ A = static_cast<const uint8_t*>(p.a);
+    const uint8_t* __restrict__ W0 = static_cast<const uint8_t*>(p.w0);
+    const uint8_t* __restrict__ W1 = static_cast<const uint8_t*>(p.w1);
+
+    for (int tau = v; tau < total; tau += G) {
+        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p.E_loc, p.offsets, cap);
+        const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
+        const int col0 = tc.nt * BNO;
+        const uint8_t* wg = W0 + (size_t)j * N * Kdim;
+        const uint8_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
+        const float* wgs = p.w0_scales + (size_t)j * N * nbK;
+        const float* wus = GATED ? p.w1_scales + (size_t)j * N * nbK : nullptr;
+
+        uint4 ra[A_IT], rb[B_IT];
+        float ras = 0.f, rbs = 0.f;
+#pragma unroll
+        for (int i = 0; i < A_IT; ++i) ra[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < B_IT; ++i) rb[i] = make_uint4(0, 0, 0, 0);
+
+        auto load_step = [&](int kb) {
+            const int k0 = kb * BKB;
+#pragma unroll
+            for (int i = 0; i < A_IT; ++i) {
+                const int q = tid + i * NT;
+                const int r = q >> 3, c = q & 7;
+                if (q < BM * 8 && r < nvalid) {
+                    ra[i] = (k0 + c * 16 < Kdim)
+                                ? *reinterpret_cast<const uint4*>(A + (size_t)(row0 + r) * Kdim + k0 + c * 16)
+                                : make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < B_IT; ++i) {
+                const int q = tid + i * NT;
+                const int r = q >> 3, c = q & 7;
+                if (q < BN * 8) {
+                    int col;
+                    const uint8_t* src;
+                    if (GATED) {
+                        const bool up = r >= BN / 2;
+                        col = col0 + (up ? r - BN / 2 : r);
+                        src = up ? wu : wg;
+                    } else {
+                        col = col0 + r;
+                        src = wg;
+                    }
+                    rb[i] = (col < N && k0 + c * 16 < Kdim)
+                                ? *reinterpret_cast<const uint4*>(src + (size_t)col * Kdim + k0 + c * 16)
+                                : make_uint4(0, 0, 0, 0);
+                }
+            }
+            // scales of this k-block: thread tid < BM loads a row scale, BM <= tid < BM+BN a column scale
+            if (tid < BM) {
+                ras = (tid < nvalid) ? p.a_scales[(size_t)(row0 + tid) * nbK + kb] : 0.f;
+            }
+            const int bt = tid - (NT - BN);           // the last BN threads load column scales
+            if (bt >= 0 && bt < BN) {
+                int col;
+                const float* sp;
+                if (GATED) {
+                    const bool up = bt >= BN / 2;
+                    col = col0 + (up ? bt - BN / 2 : bt);
+                    sp = up ? wus : wgs;
+                } else {
+                    col = col0 + bt;
+                    sp = wgs;
+                }
+                rbs = (col < N) ? sp[(size_t)col * nbK + kb] : 0.f;
+            }
+        };
+        auto store_step = [&]() {
+#pragma unroll
+            for (int i = 0; i < A_IT; ++i) {
+                const int q = tid + i * NT;
+                const int r = q >> 3, c = q & 7;
+                if (q < BM * 8 && r < nvalid) sA[r * 8 + (c ^ (r & 7))] = ra[i];
+            }
+#pragma unroll
+            for (int i = 0; i < B_IT; ++i) {
+                const int q = tid + i * NT;
+                const int r = q >> 3, c = q & 7;
+                if (q < BN * 8) sB[r * 8 + (c ^ (r & 7))] = rb[i];
+            }
+            if (tid < BM) sAs[tid] = ras;
+            const int bt = tid - (NT - BN);
+            if (bt >= 0 && bt < BN) sBs[bt] = rbs;
+        };
+
+        floatx4 acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int f = 0; f < FN; ++f) acc[i][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+        auto brow = [&](int f) {
+            if (GATED) {
+                const int half = f < FN / 2 ? 0 : BN / 2;
+                const int ff = f < FN / 2 ? f : f - FN / 2;
+                return half + wn * (WN / 2) + ff * 16 + (lane & 15);
+            }
+            return wn * WN + f * 16 + (lane & 15);
+        };
+        auto fcol = [&](int f) {
+            if (GATED) {
+                const int ff = f < FN / 2 ? f : f - FN / 2;
+                return col0 + wn * (WN / 2) + ff * 16;
+            }
+            return col0 + wn * WN + f * 16;
+        };
+
+        load_step(0);
+        for (int kb = 0; kb < nbK; ++kb) {
+            __syncthreads();
+            store_step();
+            __syncthreads();
+            if (kb + 1 < nbK) load_step(kb + 1);
+            const int c0 = 2 * (lane >> 4);
+            intx8 bfr[FN];
+            float bsc[FN];
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const int r = brow(f);
+                const uint4 t0 = sB[r * 8 + (c0 ^ (r & 7))];
+                const uint4 t1 = sB[r * 8 + ((c0 + 1) ^ (r & 7))];
+                bfr[f] = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
+                               (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
+                bsc[f] = sBs[r];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int mrow = (wm + WMW * i) * 16;
+                if (mrow < nvalid) {
+                    const int r = mrow + (lane & 15);
+                    const uint4 t0 = sA[r * 8 + (c0 ^ (r & 7))];
+                    const uint4 t1 = sA[r * 8 + ((c0 + 1) ^ (r & 7))];
+                    const intx8 afr = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
+                                            (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
+                    float asc[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) asc[e] = sAs[mrow + (lane >> 4) * 4 + e];
+#pragma unroll
+                    for (int f = 0; f < FN; ++f) {
+                        if (fcol(f) < N) {
+                            const floatx4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                            // lane l's outputs sit in column l % 16, whose scale bsc[f] holds
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[e], asc[e] * bsc[f], acc[i][f][e]);
+                        }
+                    }
+                }
+            }
+        }
+
+        // ---- epilogue
+        if constexpr (GATED) {
+            // h = silu(g) * u, then per-row amax over the tile's 128 columns
+            constexpr int FO = FN / 2;
+            float hv[FM][FO][4];
+            float rmax[FM][4];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rmax[i][e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int f = 0; f < FO; ++f)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = fcol(f) + (lane & 15) < N;
+                        const float h = ok ? silu(acc[i][f][e]) * acc[i][f + FO][e] : 0.f;
+                        hv[i][f][e] = h;
+                        rmax[i][e] = fmaxf(rmax[i][e], fabsf(h));
+                    }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float m = rmax[i][e];
+#pragma unroll
+                    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+                    if ((lane & 15) == 0) s_amax[wn][(wm + WMW * i) * 16 + (lane >> 4) * 4 + e] = m;
+                }
+            __syncthreads();
+            uint8_t* Out = static_cast<uint8_t*>(p.out);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int mrow = (wm + WMW * i) * 16;
+                if (mrow >= nvalid) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = mrow + (lane >> 4) * 4 + e;
+                    if (r >= nvalid) continue;
+                    float amax = 0.f;
+#pragma unroll
+                    for (int w = 0; w < WNW; ++w) amax = fmaxf(amax, s_amax[w][r]);
+                    const float s = amax == 0.f ? 1.f : amax / 448.0f;
+#pragma unroll
+                    for (int f = 0; f < FO; ++f) {
+                        const int col = fcol(f) + (lane & 15);
+                        if (col < N) Out[(size_t)(row0 + r) * N + col] = (uint8_t)f32_to_e4m3_sat(hv[i][f][e] / s);
+                    }
+                    if (wn == 0 && (lane & 15) == 0) p.out_scales[(size_t)(row0 + r) * nbN + tc.nt] = s;
+                }
+            }
+            __syncthreads();
+        } else {
+            uint16_t* Out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int mrow = (wm + WMW * i) * 16;
+                if (mrow >= nvalid) continue;
+#pragma unroll
+                for (int f = 0; f < FN; ++f) {
+                    const int col = fcol(f) + (lane & 15);
+                    if (col >= N) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = mrow + (lane >> 4) * 4 + e;
+                        if (r < nvalid) Out[(size_t)(row0 + r) * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][f][e]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WMW, int WNW, bool GATED>
+hipError_t launch_cfg(const FfnArgs& a, hipStream_t stream) {
+    static int per_cu = 0;
+    return launch_persistent(grouped_gemm_fp8_kernel<BM, BN, WMW, WNW, GATED>, 64 * WMW * WNW, a,
+                             stream, &per_cu);
+}
+
+}  // namespace
+
+hipError_t launch_ffn_fp8(const FfnArgs& a, bool gated, hipStream_t stream) {
+    return gated ? launch_cfg<128, 256, 2, 4, true>(a, stream)
+                 : launch_cfg<128, 128, 2, 2, false>(a, stream);
+}
+
+}  // namespace moeep

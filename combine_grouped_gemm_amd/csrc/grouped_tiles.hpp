@@ -1,0 +1,109 @@
+// Ragged tile scheduling shared by the grouped GEMM kernels.
+//
+// The per-expert row counts exist only on the device (offsets), so a
+// persistent grid derives its work list there: every block builds the
+// prefix sum over local experts of ceil(rows / BM) m-tiles in LDS and maps a
+// linear tile index tau to (expert j, n-tile, m-tile) by binary search, with
+// the m-tile index fastest so that tiles sharing one weight tile are
+// consecutive.  Blocks are renumbered XCD-major (hardware dispatch places
+// block b on XCD b % 8), so consecutive tile indices run on one XCD and
+// share its L2.
+#pragma once
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace moeep {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kXcd = 8;
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Block-wide exclusive prefix of m-tile counts per expert into s_pre[0..E_loc].
+// s_tmp needs NT / 64 ints.  Ends with a barrier.
+template <int NT, int BM>
+__device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E_loc, int cap,
+                                  int* s_pre, int* s_tmp) {
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    constexpr int NW = NT / kWave;
+    int carry = 0;
+    if (tid == 0) s_pre[0] = 0;
+    for (int base = 0; base < E_loc; base += NT) {
+        const int j = base + tid;
+        int v = 0;
+        if (j < E_loc) {
+            const int r0 = clampi(offsets[j], 0, cap), r1 = clampi(offsets[j + 1], 0, cap);
+            const int n = r1 > r0 ? r1 - r0 : 0;
+            v = (n + BM - 1) / BM;
+        }
+        int x = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            int y = __shfl_up(x, d, kWave);
+            if (lane >= d) x += y;
+        }
+        if (lane == kWave - 1) s_tmp[wv] = x;
+        __syncthreads();
+        int wsum = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            wsum += (w < wv) ? s_tmp[w] : 0;
+            total += s_tmp[w];
+        }
+        if (j < E_loc) s_pre[j + 1] = carry + wsum + x;
+        carry += total;
+        __syncthreads();
+    }
+    __syncthreads();
+}
+
+struct TileCoord {
+    int j;        // local expert
+    int nt;       // n-tile
+    int row0;     // first row of the tile
+    int nvalid;   // valid rows in the tile (<= BM)
+};
+
+template <int BM>
+__device__ __forceinline__ TileCoord decode_tile(int tau, int n_tiles_n, const int* s_pre,
+                                                 int E_loc, const int32_t* __restrict__ offsets,
+                                                 int cap) {
+    int lo = 0, hi = E_loc;       // largest j with n_tiles_n * s_pre[j] <= tau
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (n_tiles_n * s_pre[mid] <= tau) lo = mid; else hi = mid;
+    }
+    TileCoord t;
+    t.j = lo;
+    const int mt_j = s_pre[lo + 1] - s_pre[lo];
+    const int local = tau - n_tiles_n * s_pre[lo];
+    t.nt = local / mt_j;
+    const int mt = local % mt_j;
+    const int r0 = clampi(offsets[lo], 0, cap), r1 = clampi(offsets[lo + 1], 0, cap);
+    t.row0 = r0 + mt * BM;
+    t.nvalid = min(BM, r1 - t.row0);
+    return t;
+}
+
+// XCD-major renumbering of the block index (identity when G % 8 != 0).
+__device__ __forceinline__ int xcd_block_order() {
+    const int G = gridDim.x, b = blockIdx.x;
+    return (G % kXcd == 0) ? (b % kXcd) * (G / kXcd) + b / kXcd : b;
+}
+
+template <typename Kern>
+hipError_t launch_persistent(Kern kern, int threads, const FfnArgs& a, hipStream_t stream,
+                             int* per_cu_cache) {
+    if (*per_cu_cache == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess || n < 1)
+            n = 1;
+        *per_cu_cache = n;
+    }
+    const int grid = device_cu_count() * *per_cu_cache;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace moeep

@@ -1,0 +1,201 @@
+// Expert-contiguous layout of the routed slots: histogram, exclusive scan,
+// stable permutation.
+//
+// "Anatomy of a high-performance EP kernel", section "Dispatch": each expert
+// receives its own number of rows and the grouped GEMM runs over one row set
+// per expert; SGLang "Expert Parallelism", "Framework Overview": the
+// pre-permute stage in front of the grouped GEMM.
+//
+// The flattened slots s = t*K + k are cut into chunks of kChunk.  Three
+// kernels, all deterministic (no arrival-order dependence):
+//   1. hist:  one wave per chunk walks it 64 slots at a time; lanes holding
+//             the same expert find each other with a ballot per id bit
+//             (match mask), the lowest such lane adds the group size to an
+//             LDS histogram.  The chunk histogram goes to the workspace.
+//   2. scan:  one block; per expert an exclusive scan over chunks (so chunk
+//             c knows how many earlier slots share its experts), the totals
+//             become `counts`, an exclusive scan over the local experts
+//             gives `offsets`, and every chunk's entry becomes its first
+//             destination row.
+//   3. rank:  the same walk as 1; a slot's row is its chunk's running base
+//             for the expert plus the number of lower lanes holding the same
+//             expert, which keeps rows of an expert in ascending slot order.
+//             Also fills src_of's padding rows with -1.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace moeep {
+namespace {
+
+constexpr int kChunk = 1024;        // slots per chunk (16 wave steps)
+constexpr int kScanThreads = 1024;  // >= the largest E
+
+struct LayoutWs {
+    int32_t* base;    // [nchunk][E]: chunk histogram, then first row per (chunk, local expert)
+    int32_t* total;   // 1 int: local rows R
+};
+
+__host__ __device__ inline int n_chunks(long long slots) {
+    return (int)((slots + kChunk - 1) / kChunk);
+}
+
+inline LayoutWs carve(void* ws, int nchunk, int E) {
+    LayoutWs w;
+    w.base = static_cast<int32_t*>(ws);
+    w.total = w.base + (size_t)nchunk * E;
+    return w;
+}
+
+__device__ __forceinline__ int id_bits(int E) { return E <= 1 ? 1 : 32 - __clz(E - 1); }
+
+__global__ __launch_bounds__(kWave) void layout_hist_kernel(const int32_t* __restrict__ ids,
+                                                            int n_slots, int E,
+                                                            int32_t* __restrict__ base) {
+    extern __shared__ int32_t s_hist[];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += kWave) s_hist[e] = 0;
+    __syncthreads();
+    const int nbits = id_bits(E);
+    const int s0 = blockIdx.x * kChunk;
+    for (int step = 0; step < kChunk; step += kWave) {
+        const int s = s0 + step + lane;
+        int e = (s < n_slots) ? ids[s] : -1;
+        const bool valid = e >= 0 && e < E;
+        const uint64_t active = ballot64(valid);
+        if (active != 0) {                           // wave-uniform
+            const uint64_t m = match_mask((uint32_t)(valid ? e : 0), active, nbits);
+            if (valid && (m & lanemask_lt()) == 0) s_hist[e] += popc64(m);
+        }
+        __syncthreads();
+    }
+    __syncthreads();
+    int32_t* out = base + (size_t)blockIdx.x * E;
+    for (int e = lane; e < E; e += kWave) out[e] = s_hist[e];
+}
+
+__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
+    int nchunk, int E, int e_begin, int e_end, int32_t* __restrict__ base,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ total) {
+    __shared__ int32_t s_cnt[kScanThreads];
+    __shared__ int32_t s_wave[kScanThreads / kWave];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int c = 0; c < nchunk; ++c) {
+            int32_t* p = base + (size_t)c * E + e;
+            const int v = *p;
+            *p = run;
+            run += v;
+        }
+        counts[e] = run;
+    }
+    // exclusive scan of counts over the local experts, thread j <-> expert e_begin + j
+    const int j = threadIdx.x;
+    const int E_loc = e_end - e_begin;
+    s_cnt[j] = 0;
+    __syncthreads();
+    if (e < E && e >= e_begin && e < e_end) s_cnt[e - e_begin] = run;
+    __syncthreads();
+    // inclusive scan within each wave, then across waves
+    int x = s_cnt[j];
+    const int lane = j % kWave, wv = j / kWave;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) s_wave[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+        int t = (lane < kScanThreads / kWave) ? s_wave[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            int y = __shfl_up(t, d, kWave);
+            if (lane >= d) t += y;
+        }
+        if (lane < kScanThreads / kWave) s_wave[lane] = t;
+    }
+    __syncthreads();
+    const int incl = x + (wv > 0 ? s_wave[wv - 1] : 0);
+    const int excl = incl - s_cnt[j];
+    if (j < E_loc) offsets[j] = excl;
+    if (j == E_loc - 1) {
+        offsets[E_loc] = incl;
+        *total = incl;
+    }
+    __syncthreads();
+    s_cnt[j] = excl;               // reuse as the local exclusive offsets
+    __syncthreads();
+    if (e < E && e >= e_begin && e < e_end) {
+        const int off = s_cnt[e - e_begin];
+        for (int c = 0; c < nchunk; ++c) base[(size_t)c * E + e] += off;
+    }
+}
+
+__global__ __launch_bounds__(kWave) void layout_rank_kernel(
+    const int32_t* __restrict__ ids, int n_slots, int E, int e_begin, int e_end, int cap,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ total,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of) {
+    extern __shared__ int32_t s_next[];
+    const int lane = threadIdx.x;
+    const int E_loc = e_end - e_begin;
+    const int s0 = blockIdx.x * kChunk;
+    const int steps = s0 < n_slots ? kChunk : 0;     // an empty input still pads src_of
+    if (steps > 0) {
+        const int32_t* my = base + (size_t)blockIdx.x * E + e_begin;
+        for (int j = lane; j < E_loc; j += kWave) s_next[j] = my[j];
+    }
+    __syncthreads();
+    const int nbits = id_bits(E);
+    for (int step = 0; step < steps; step += kWave) {
+        const int s = s0 + step + lane;
+        const bool in = s < n_slots;
+        const int e = in ? ids[s] : -1;
+        const bool local = e >= e_begin && e < e_end;
+        const uint64_t active = ballot64(local);
+        int row = -1;
+        if (active != 0) {                            // wave-uniform
+            const uint64_t m = match_mask((uint32_t)(local ? e - e_begin : 0), active, nbits);
+            if (local) {
+                const int rank = popc64(m & lanemask_lt());
+                const int r = s_next[e - e_begin] + rank;
+                row = r < cap ? r : -1;
+                if (row >= 0) src_of[row] = s;
+                if (rank == 0) s_next[e - e_begin] = r + popc64(m);
+            }
+        }
+        if (in) row_of[s] = row;
+        __syncthreads();
+    }
+    // padding rows of src_of
+    const int R = *total;
+    for (int r = R + blockIdx.x * kWave + lane; r < cap; r += gridDim.x * kWave) src_of[r] = -1;
+}
+
+}  // namespace
+
+size_t layout_workspace_bytes(int B, int K, int E) {
+    const int nchunk = n_chunks((long long)B * K);
+    size_t bytes = ((size_t)nchunk * E + 1) * sizeof(int32_t);
+    return (bytes + 255) / 256 * 256;
+}
+
+hipError_t launch_layout(const int32_t* ids, int B, int K, int E, int e_begin, int e_end,
+                         int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                         int cap, void* ws, hipStream_t stream) {
+    const int n_slots = B * K;
+    const int nchunk = n_chunks(n_slots);
+    LayoutWs w = carve(ws, nchunk, E);
+    if (nchunk > 0) {
+        hipLaunchKernelGGL(layout_hist_kernel, dim3(nchunk), dim3(kWave), E * sizeof(int32_t),
+                           stream, ids, n_slots, E, w.base);
+    }
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, nchunk, E,
+                       e_begin, e_end, w.base, counts, offsets, w.total);
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(nchunk > 0 ? nchunk : 1), dim3(kWave),
+                       (e_end - e_begin) * sizeof(int32_t), stream, ids, n_slots, E, e_begin,
+                       e_end, cap, w.base, w.total, row_of, src_of);
+    return hipGetLastError();
+}
+
+}  // namespace moeep

@@ -1,0 +1,95 @@
+"""One GPU's share of the expert-parallel MoE layer, with its buffers
+allocated once (capacity-sized, so every call has static sizes and no host
+synchronisation, the property the Moreh report's "Using HIP Graphs" section
+asks of an EP decode step).
+
+    route -> layout -> dispatch -> gate/up (+SwiGLU) -> down -> combine
+
+Every stage is one call into libmoeep; this class only owns the buffers
+and orders the calls on one stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (FP8_BLOCK, moe_combine, moe_dispatch, moe_ffn_down, moe_ffn_gate_up,
+               moe_layout, moe_layout_workspace_bytes, moe_route)
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+
+
+class MoELayer:
+    """Buffers and stage order for one layer shape.
+
+    seg_rows: tokens per simulated source segment (T = sum); E routed experts,
+    K per token; H hidden, I expert intermediate; local experts
+    [e_begin, e_end); act_dtype stores Xd and h ('f32' | 'bf16' | 'fp8');
+    y_dtype / out_dtype store the expert outputs and the combined rows.
+    """
+
+    def __init__(self, seg_rows, E, K, H, I, e_begin, e_end, act_dtype, y_dtype, out_dtype,
+                 device="cuda", cap_rows=None):
+        self.seg_rows = tuple(int(b) for b in seg_rows)
+        self.T = sum(self.seg_rows)
+        self.E, self.K, self.H, self.I = E, K, H, I
+        self.e_begin, self.e_end = e_begin, e_end
+        self.E_loc = e_end - e_begin
+        self.act_dtype, self.y_dtype, self.out_dtype = act_dtype, y_dtype, out_dtype
+        self.cap = self.T * K if cap_rows is None else int(cap_rows)
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        T, cap = self.T, max(self.cap, 1)
+        self.topk_ids = torch.empty((T, K), **i32)
+        self.topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(self.E_loc + 1, **i32)
+        self.row_of = torch.empty((T, K), **i32)
+        self.src_of = torch.empty(cap, **i32)
+        self.layout_ws = torch.empty(max(moe_layout_workspace_bytes(T, K, E), 256),
+                                     dtype=torch.uint8, device=dev)
+        act = _TORCH[act_dtype]
+        self.xd = torch.empty((cap, H), dtype=act, device=dev)
+        self.h = torch.empty((cap, I), dtype=act, device=dev)
+        fp8 = act_dtype == "fp8"
+        self.xd_scales = torch.empty((cap, -(-H // FP8_BLOCK)), dtype=torch.float32, device=dev) if fp8 else None
+        self.h_scales = torch.empty((cap, -(-I // FP8_BLOCK)), dtype=torch.float32, device=dev) if fp8 else None
+        self.y = torch.empty((cap, H), dtype=_TORCH[y_dtype], device=dev)
+        self.out = torch.empty((T, H), dtype=_TORCH[out_dtype], device=dev)
+
+    # individual stages (each one library call) ---------------------------------
+    def route(self, logits, stream=None):
+        moe_route(logits, self.K, self.topk_ids, self.topk_w, stream=stream)
+
+    def layout(self, stream=None):
+        moe_layout(self.topk_ids, self.E, self.e_begin, self.e_end, self.cap, self.counts,
+                   self.offsets, self.row_of, self.src_of, self.layout_ws, stream=stream)
+
+    def dispatch(self, x_segments, stream=None):
+        moe_dispatch(x_segments, self.row_of, self.cap, self.act_dtype, self.xd, self.xd_scales,
+                     stream=stream)
+
+    def gate_up(self, w, stream=None):
+        moe_ffn_gate_up(self.xd, self.xd_scales, self.offsets, w["gate"], w["up"],
+                        w.get("gate_scale"), w.get("up_scale"), self.h, self.h_scales,
+                        stream=stream)
+
+    def down(self, w, stream=None):
+        moe_ffn_down(self.h, self.h_scales, self.offsets, w["down"], w.get("down_scale"), self.y,
+                     stream=stream)
+
+    def combine(self, stream=None):
+        moe_combine(self.y, self.row_of, self.topk_w, self.out, stream=stream)
+
+    def stages(self, x_segments, logits, w):
+        """(name, thunk) pairs of the six calls, in order."""
+        return [("route", lambda s=None: self.route(logits, s)),
+                ("layout", lambda s=None: self.layout(s)),
+                ("dispatch", lambda s=None: self.dispatch(x_segments, s)),
+                ("ffn_gate_up", lambda s=None: self.gate_up(w, s)),
+                ("ffn_down", lambda s=None: self.down(w, s)),
+                ("combine", lambda s=None: self.combine(s))]
+
+    def forward(self, x_segments, logits, w, stream=None):
+        for _, run in self.stages(x_segments, logits, w):
+            run(stream)
+        return self.out

@@ -1,0 +1,204 @@
+/*
+ * moeep.h -- C ABI of libmoeep, the single-GPU data-parallel path of an
+ * expert-parallel Mixture-of-Experts layer on AMD Instinct MI355X (gfx950):
+ *
+ *     route -> layout -> dispatch -> grouped SwiGLU FFN -> combine
+ *
+ * Sources, cited by page title and section:
+ *   [Anatomy]  "Anatomy of a high-performance EP kernel" (euno.news, Korean;
+ *              Chinese translation on 66bd.net), section "What we have to
+ *              do" and its router figure, section "Dispatch".
+ *   [Moreh]    Moreh, "21K output tokens/s DeepSeek inference on AMD
+ *              Instinct MI300X GPUs with Expert Parallelism", sections
+ *              "Parallelisation method", "Load balancing across GPUs",
+ *              "Using HIP Graphs".
+ *   [SGLang]   SGLang documentation, "Expert Parallelism", section
+ *              "Framework Overview" (the dispatch -> pre-permute -> grouped
+ *              GEMM -> post-permute -> combine flow) and the MoE-runner
+ *              backend table (contiguous layout, fp8 block quantisation).
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers to caller-owned memory unless
+ *     marked "host".  Tensors are row-major and dense.  The library never
+ *     allocates, frees, synchronises or copies device->host; every call only
+ *     enqueues kernels on `stream` (0 = the null stream) and returns.
+ *   - Arguments are checked on the host before anything is enqueued.  A
+ *     non-OK status means nothing was enqueued and no output was touched;
+ *     moe_last_error() then holds a message (thread-local).
+ *   - MOE_ERR_HIP reports a failed kernel launch.  Faults inside a kernel
+ *     surface, as always with HIP, at the caller's next synchronisation.
+ *   - Sizes: 1 <= K <= E <= 1024; 0 <= e_begin < e_end <= E; B >= 0;
+ *     H and I multiples of 64; row base pointers 16-byte aligned.
+ *   - Calls on one stream run in order; calls that share output or
+ *     workspace buffers on different streams race.
+ *   - Expert ids outside [0, E) in topk_ids are treated as unrouted slots.
+ *   - Non-finite logits or activations are outside the method; results
+ *     are then unspecified (but all memory accesses stay in bounds).
+ */
+#ifndef MOEEP_H
+#define MOEEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* a pointer, size or alignment check failed */
+    MOE_ERR_UNSUPPORTED = 2,   /* a valid but unimplemented dtype/shape combination */
+    MOE_ERR_HIP = 3            /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_FP8_E4M3 = 2           /* OCP e4m3fn (finite max 448), with fp32 1x128 block scales */
+} moe_dtype_t;
+
+/* Largest number of simulated source segments moe_dispatch accepts. */
+#define MOE_MAX_SEGMENTS 64
+/* fp8 scale block length along the contraction (row) dimension. */
+#define MOE_FP8_BLOCK 128
+
+const char* moe_status_string(moe_status_t status);
+const char* moe_last_error(void);
+const char* moe_version(void);
+
+/*
+ * moe_route -- top-K expert selection and gate weights.
+ * [Anatomy] "What we have to do": each token's (E) logit row is reduced to
+ * the indices of its K largest logits, a (B, K) assignment tensor.  Gate
+ * weights are the softmax over the K selected logits (the full softmax
+ * renormalised over the picks).
+ *
+ *   logits   (B, E) fp32, finite.
+ *   topk_ids (B, K) int32 out: slot k holds the k-th largest logit; equal
+ *            logits are taken in ascending expert id (-0.0 equals +0.0).
+ *   topk_w   (B, K) fp32 out: exp(l_k - l_0) / sum_j exp(l_j - l_0).
+ * B = 0 is a no-op.
+ */
+moe_status_t moe_route(const float* logits, int B, int E, int K,
+                       int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/*
+ * moe_layout -- per-expert histogram, exclusive prefix sum and permutation
+ * of the routed slots into expert-contiguous rows.  [Anatomy] "Dispatch":
+ * each expert receives its own number of rows and the grouped GEMM runs
+ * over one row set per expert; [SGLang] "Framework Overview": pre-permute.
+ *
+ *   topk_ids (B, K) int32.
+ *   counts   (E) int32 out: slots routed to each of the E experts.
+ *   offsets  (e_end - e_begin + 1) int32 out: exclusive scan of counts over
+ *            the local experts [e_begin, e_end), total last.  Local expert j
+ *            (global id e_begin + j) owns rows [offsets[j], offsets[j+1]).
+ *   row_of   (B, K) int32 out: destination row of slot (t, k), -1 if its
+ *            expert is not local.
+ *   src_of   (cap_rows) int32 out: slot t*K + k held by each row; -1 for the
+ *            rows [offsets[E_loc], cap_rows).
+ *   Rows of one expert are ordered by (t, k) ascending, so the result is
+ *   deterministic and bit-identical run to run.
+ *   cap_rows >= B * K * (fraction routed locally); B * K always suffices.
+ *   If more local slots than cap_rows arrive, the rows past cap_rows are
+ *   dropped: their row_of is -1 and offsets still count them.
+ *   ws / ws_bytes: device workspace of at least
+ *   moe_layout_workspace_bytes(B, K, E) bytes, 256-byte aligned.
+ */
+size_t moe_layout_workspace_bytes(int B, int K, int E);
+moe_status_t moe_layout(const int32_t* topk_ids, int B, int K, int E, int e_begin, int e_end,
+                        int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                        int cap_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch -- scatter token rows into the dense expert-contiguous
+ * buffer that feeds the grouped GEMM.  [Anatomy] "Dispatch": the tokens for
+ * the local experts are gathered into one dense buffer so the grouped GEMM
+ * takes them in one call.  On one GPU the transport is an HBM copy; the
+ * tokens arrive from n_seg simulated source ranks ([Anatomy] "What we have
+ * to do": every data-parallel rank holds its own (B_i, H) activations).
+ *
+ *   seg_x    host array of n_seg device pointers, segment i is (seg_rows[i], H)
+ *            of x_dt.  Global token t is the segment-major concatenation.
+ *   seg_rows host array of n_seg row counts (B = their sum).
+ *   row_of   (B, K) int32 from moe_layout.
+ *   xd       (cap_rows, H) of xd_dt out: xd[row_of[t,k]] = x[t] for every
+ *            local slot.  Rows not named by row_of are not written.
+ *   xd_scales (cap_rows, ceil(H/128)) fp32 out, fp8 only (else may be NULL).
+ * Supported (x_dt -> xd_dt): F32 -> F32 and BF16 -> BF16 (bit-exact
+ * copies); BF16 -> FP8_E4M3 (each token quantised once: per 128-element
+ * block s = amax/448 (1 if amax = 0), code = RNE(v/s) saturated to +-448,
+ * with fp32 arithmetic; all K copies carry identical codes and scales).
+ */
+moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int n_seg,
+                          moe_dtype_t x_dt, int H, const int32_t* row_of, int K,
+                          void* xd, moe_dtype_t xd_dt, float* xd_scales,
+                          int cap_rows, hipStream_t stream);
+
+/*
+ * Grouped SwiGLU expert FFN.  [Moreh] "Overview": experts are small FFN
+ * layers; [Anatomy] "Dispatch": one grouped GEMM over a separate row set
+ * per expert; [SGLang] MoE-runner table: contiguous (prefill) layout and
+ * fp8 block-wise quantisation.  For each local expert j and its rows
+ * [offsets[j], offsets[j+1]) of xd:
+ *     g = Xd W_gate[j]^T,  u = Xd W_up[j]^T   (fp32 accumulation)
+ *     h = silu(g) * u                          stored as act_dt
+ *     y = h W_down[j]^T                        (fp32 accumulation) stored as y_dt
+ * Weights use the (out, in) layout: w_gate, w_up (E_local, I, H);
+ * w_down (E_local, H, I), local expert j first.  fp8 weights carry fp32
+ * scales per (output row, 128-wide block of the input dim):
+ * w_gate_scales, w_up_scales (E_local, I, ceil(H/128)),
+ * w_down_scales (E_local, H, ceil(I/128)).  fp8 activations carry
+ * xd_scales (cap_rows, ceil(H/128)) and h_scales (cap_rows, ceil(I/128)).
+ * h is quantised like the dispatched activations.  Rows past
+ * offsets[E_local] of h and y are not written.
+ *
+ * Supported (act_dt, w_dt, y_dt): (F32, F32, F32), (BF16, BF16, BF16),
+ * (FP8_E4M3, FP8_E4M3, BF16).
+ *
+ * moe_ffn_gate_up computes h; moe_ffn_down computes y from h;
+ * moe_grouped_ffn runs both with h (and h_scales) carved from `ws`, which
+ * must hold moe_ffn_workspace_bytes(cap_rows, I, act_dt) bytes.
+ * The row counts per expert are read on the device: no host
+ * synchronisation, launch sizes depend only on the arguments.
+ */
+size_t moe_ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt);
+moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32_t* offsets,
+                             int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
+                             const void* w_gate, const void* w_up,
+                             const float* w_gate_scales, const float* w_up_scales, moe_dtype_t w_dt,
+                             void* h, float* h_scales, hipStream_t stream);
+moe_status_t moe_ffn_down(const void* h, const float* h_scales, const int32_t* offsets,
+                          int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
+                          const void* w_down, const float* w_down_scales, moe_dtype_t w_dt,
+                          void* y, moe_dtype_t y_dt, hipStream_t stream);
+moe_status_t moe_grouped_ffn(const void* xd, const float* xd_scales, const int32_t* offsets,
+                             int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const float* w_gate_scales, const float* w_up_scales,
+                             const float* w_down_scales, moe_dtype_t w_dt,
+                             void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * moe_combine -- gate-weighted gather-reduce back to token order.
+ * [Anatomy] the paragraph after the router figure: results go back to
+ * where their tokens live; [SGLang] "Framework Overview": post-permute and
+ * combine.  out[t] = sum over k with row_of[t,k] >= 0, in ascending k, of
+ * topk_w[t,k] * y[row_of[t,k]], accumulated in fp32 and rounded once to
+ * out_dt (RNE).  Tokens with no local slot get 0.  With only part of the
+ * experts local this is the rank's partial sum.
+ *   y (cap_rows, H) y_dt; row_of, topk_w (B, K); out (B, H) out_dt.
+ *   Rows named by row_of outside [0, cap_rows) are skipped like -1.
+ * Supported (y_dt, out_dt): (F32, F32), (BF16, BF16), (BF16, F32).
+ */
+moe_status_t moe_combine(const void* y, moe_dtype_t y_dt, int cap_rows, const int32_t* row_of,
+                         const float* topk_w, int B, int K, int H,
+                         void* out, moe_dtype_t out_dt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEEP_H */

@@ -1,0 +1,105 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_grouped_gemm_amd as m
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moeep.h")
+
+
+def declared():
+    text = open(HDR).read()
+    return re.findall(r"^\s*(?:moe_status_t|size_t|const char\*)\s+(moe_\w+)\(", text, re.M)
+
+
+def test_exports_every_declared_symbol():
+    L = m.lib()
+    names = declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = m.lib()
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(3) == b"MOE_ERR_HIP"
+    assert b"gfx950" in L.moe_version()
+
+
+BAD_ROUTE = [((None, 4, 0, 1), "E must be"), ((None, 4, 8, 9), "K must be"),
+             ((None, -1, 8, 2), "B must be"), ((None, 4, 2000, 2), "E must be"),
+             ((None, 4, 8, 2), "null pointer")]
+
+
+@pytest.mark.parametrize("args,msg", BAD_ROUTE)
+def test_route_rejects(args, msg):
+    L = m.lib()
+    assert L.moe_route(*args, None, None, None) == m.MOE_ERR_INVALID_ARG
+    assert msg in L.moe_last_error().decode()
+
+
+def test_route_empty_batch_is_noop():
+    assert m.lib().moe_route(None, 0, 8, 2, None, None, None) == m.MOE_OK
+
+
+def test_layout_rejects():
+    L = m.lib()
+    p = ctypes.c_void_p(256)       # never dereferenced: every case fails its host check first
+    assert L.moe_layout(p, 4, 2, 8, 3, 3, p, p, p, p, 8, p, 1 << 20, None) == m.MOE_ERR_INVALID_ARG
+    assert "e_begin" in L.moe_last_error().decode()
+    assert L.moe_layout(p, 4, 2, 8, 0, 8, p, p, p, p, 8, ctypes.c_void_p(257), 1 << 20, None) == 1
+    assert "256-byte" in L.moe_last_error().decode()
+    assert L.moe_layout(p, 4, 2, 8, 0, 8, p, p, p, p, 8, p, 4, None) == m.MOE_ERR_INVALID_ARG
+    assert "workspace too small" in L.moe_last_error().decode()
+    assert L.moe_layout_workspace_bytes(8192, 8, 256) % 256 == 0
+
+
+def test_dispatch_rejects():
+    L = m.lib()
+    p = ctypes.c_void_p(4096)
+    ptrs = (ctypes.c_void_p * 1)(4096)
+    rows = (ctypes.c_int32 * 1)(4)
+    P = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert L.moe_dispatch(P(ptrs), P(rows), 0, 1, 128, p, 2, p, 1, None, 8, None) == 1
+    assert L.moe_dispatch(P(ptrs), P(rows), 1, 1, 100, p, 2, p, 1, None, 8, None) == 1   # H % 64
+    assert L.moe_dispatch(P(ptrs), P(rows), 1, 0, 128, p, 2, p, 2, None, 8, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_dispatch(P(ptrs), P(rows), 1, 1, 128, p, 2, p, 2, None, 8, None) == 1   # fp8 needs scales
+    ptrs[0] = 4097
+    assert L.moe_dispatch(P(ptrs), P(rows), 1, 1, 128, p, 2, p, 1, None, 8, None) == 1   # misaligned
+    assert "aligned" in L.moe_last_error().decode()
+
+
+def test_ffn_rejects():
+    L = m.lib()
+    p = ctypes.c_void_p(4096)
+    # bf16 activations with fp8 weights: unsupported
+    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 1, p, p, None, None, 2, p, None, None) == 2
+    # I not a multiple of 64
+    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 100, 1, p, p, None, None, 1, p, None, None) == 1
+    # fp8 without scales
+    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 2, p, p, None, None, 2, p, None, None) == 1
+    # fp8 activations need a bf16 y
+    assert L.moe_ffn_down(p, p, p, 8, 64, 128, 128, 2, p, p, 2, p, 2, None) == 2
+    # workspace too small
+    assert L.moe_grouped_ffn(p, None, p, 8, 64, 128, 128, 1, p, p, p, None, None, None, 1, p, 1,
+                             p, 16, None) == 1
+    assert L.moe_ffn_workspace_bytes(64, 128, 2) >= 64 * 128 + 64 * 4
+
+
+def test_combine_rejects():
+    L = m.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.moe_combine(p, 2, 8, p, p, 4, 2, 128, p, 1, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(p, 1, 8, p, p, 4, 2, 120, p, 1, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(p, 1, 8, None, p, 4, 2, 128, p, 1, None) == m.MOE_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        m.moe_route(torch.zeros(4, 8), 2)

@@ -1,0 +1,210 @@
+"""GPU parity: every stage of the HIP path against the oracle.
+
+Integer outputs (ids, counts, offsets, row_of, src_of) and plain copies
+(bf16 / fp32 dispatch) must be bit-exact; fp8 dispatch must reproduce the
+oracle's codes and scales exactly (both take the quantisation decision in
+fp32); floating outputs must meet the layer's tolerance (bf16: relative L2
+<= 1e-2 and max-abs <= 5e-2; fp8: relative L2 <= 3e-2; fp32: 1e-5 / 1e-4).
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from harness import Case, TOL, assert_close, gpu_view, has_gpu, run_gpu, to_np
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+C = wl.CONFIGS
+SMALL = [
+    C["toy"],
+    wl.scaled(C["dsv3_decode"], "decode_small", seg_rows=(40,), E=32, K=4, H=512, I=256),
+    wl.scaled(C["dsv3_prefill"], "prefill_small", seg_rows=(600,), E=8, K=2, H=384, I=320),
+    wl.scaled(C["dsv3_prefill"], "prefill_ntail", seg_rows=(333,), E=6, K=2, H=448, I=192),
+    wl.scaled(C["ep8_share"], "ep_small", seg_rows=(100, 37, 64), E=16, K=3, H=256, I=128,
+              e_begin=4, e_end=10),
+    wl.scaled(C["gptoss_fp8"], "fp8_small", seg_rows=(300,), E=8, K=2, H=320, I=192),
+    wl.scaled(C["gptoss_fp8"], "fp8_decode_real_dims", seg_rows=(24,), E=16, K=4),
+]
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def check_exact_stages(g, o, act):
+    np.testing.assert_array_equal(g["ids"], o["ids"])
+    np.testing.assert_allclose(g["gates"], o["gates"], rtol=1e-5, atol=1e-7)
+    np.testing.assert_array_equal(g["counts"], o["counts"])
+    np.testing.assert_array_equal(g["offsets"], o["offsets"])
+    np.testing.assert_array_equal(g["row_of"], o["row_of"])
+    np.testing.assert_array_equal(g["src_of"], o["src_of"])
+    R = g["R"]
+    np.testing.assert_array_equal(g["xd"], o["xd"][:R])
+    if act == "fp8":
+        np.testing.assert_array_equal(g["xd_scales"], o["xd_scales"][:R])
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_layer_parity_small(cfg):
+    print(f"[parity] {cfg.name} T={cfg.T} E={cfg.E} K={cfg.K} H={cfg.H} I={cfg.I}", flush=True)
+    case = Case(cfg)
+    layer = run_gpu(case)
+    g = gpu_view(layer)
+    o = case.oracle_layer()
+    check_exact_stages(g, o, cfg.act_dtype)
+    assert_close(g["y"], o["y"], cfg.act_dtype, "y")
+    assert_close(g["out"], o["out"], cfg.act_dtype, "out")
+    del case, layer
+    _free()
+
+
+def _forced_case(cfg, logits):
+    case = Case(cfg)
+    case.logits_cpu = torch.as_tensor(logits, dtype=torch.float32)
+    case.logits_dev = case.logits_cpu.cuda()
+    return case
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+def test_all_tokens_one_expert_rest_empty(act):
+    base = C["dsv3_prefill"] if act == "bf16" else C["gptoss_fp8"]
+    cfg = wl.scaled(base, f"one_expert_{act}", seg_rows=(300,), E=8, K=1, H=256, I=192)
+    lg = np.random.default_rng(0).normal(size=(300, 8)).astype(np.float32)
+    lg[:, 5] += 100.0                      # every token picks expert 5: 300 rows, 7 empty
+    case = _forced_case(cfg, lg)
+    g = gpu_view(run_gpu(case))
+    o = case.oracle_layer()
+    assert o["counts"][5] == 300 and (o["counts"] == 0).sum() == 7
+    check_exact_stages(g, o, act)
+    assert_close(g["y"], o["y"], act, "y")
+    assert_close(g["out"], o["out"], act, "out")
+
+
+def test_k_equals_e_and_ties():
+    cfg = wl.scaled(C["dsv3_prefill"], "k_eq_e", seg_rows=(50,), E=4, K=4, H=128, I=64)
+    lg = np.random.default_rng(1).integers(-1, 2, size=(50, 4)).astype(np.float32)
+    case = _forced_case(cfg, lg)
+    g = gpu_view(run_gpu(case))
+    o = case.oracle_layer()
+    check_exact_stages(g, o, "bf16")
+    assert_close(g["out"], o["out"], "bf16", "out")
+
+
+def test_route_ties_and_negative_zero():
+    from combine_grouped_gemm_amd import moe_route
+    rng = np.random.default_rng(2)
+    for E, K in ((16, 2), (64, 8), (256, 8), (200, 17), (1024, 5), (7, 7)):
+        lg = rng.integers(-1, 2, size=(257, E)).astype(np.float32)
+        lg[0, :] = 0.0
+        lg[1, ::2] = -0.0
+        ids, w = moe_route(torch.from_numpy(lg).cuda(), K)
+        oi, ow = oracle.route(lg, K)
+        np.testing.assert_array_equal(ids.cpu().numpy(), oi)
+        np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-7)
+
+
+def test_empty_batch():
+    cfg = wl.scaled(C["dsv3_prefill"], "empty", seg_rows=(0,), E=8, K=2, H=128, I=64)
+    from combine_grouped_gemm_amd import MoELayer
+    layer = MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, 0, cfg.E, "bf16", "bf16", "bf16")
+    x = [torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda")]
+    lg = torch.empty((0, cfg.E), dtype=torch.float32, device="cuda")
+    w = wl.gen_expert_weights(cfg, "cuda")
+    layer.forward(x, lg, {"gate": w.gate, "up": w.up, "down": w.down})
+    torch.cuda.synchronize()
+    assert layer.counts.cpu().sum() == 0 and int(layer.offsets[-1]) == 0
+
+
+def test_capacity_overflow_drops_late_rows():
+    """cap_rows below the routed rows: the first cap rows are the oracle's,
+    later slots get row -1, and every kernel stays within the buffers."""
+    cfg = wl.scaled(C["dsv3_prefill"], "overflow", seg_rows=(64,), E=4, K=2, H=128, I=64)
+    case = Case(cfg)
+    from combine_grouped_gemm_amd import MoELayer
+    cap = 50
+    layer = MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, 0, cfg.E, "bf16", "bf16", "bf16",
+                     cap_rows=cap)
+    run_gpu(case, layer)
+    o = oracle.layout(oracle.route(case.logits_np(), cfg.K)[0], cfg.E, 0, cfg.E, cfg.T * cfg.K)
+    np.testing.assert_array_equal(layer.src_of.cpu().numpy(), o["src_of"][:cap])
+    ro = layer.row_of.cpu().numpy()
+    np.testing.assert_array_equal(ro, np.where(o["row_of"] < cap, o["row_of"], -1))
+    np.testing.assert_array_equal(layer.offsets.cpu().numpy(), o["offsets"])
+
+
+def test_deterministic_and_stage_split_matches_grouped_call():
+    from combine_grouped_gemm_amd import moe_grouped_ffn
+    cfg = wl.scaled(C["dsv3_prefill"], "det", seg_rows=(400,), E=8, K=2, H=256, I=192)
+    case = Case(cfg)
+    l1 = run_gpu(case)
+    a = {k: v.clone() for k, v in (("y", l1.y), ("out", l1.out), ("xd", l1.xd))}
+    run_gpu(case, l1)
+    assert torch.equal(a["out"], l1.out) and torch.equal(a["y"], l1.y)
+    y2 = moe_grouped_ffn(l1.xd, None, l1.offsets, case.w.gate, case.w.up, case.w.down)
+    torch.cuda.synchronize()
+    R = int(l1.offsets[-1])
+    assert torch.equal(y2[:R], l1.y[:R])
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes: exact checks on everything integer, sampled FP checks
+# ----------------------------------------------------------------------------
+FULL = ["dsv3_decode", "dsv3_prefill", "ep8_share", "gptoss_fp8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = C[name]
+    print(f"[parity-full] {name} T={cfg.T}", flush=True)
+    case = Case(cfg)
+    layer = run_gpu(case)
+    lg = case.logits_np()
+    ids, gates = oracle.route(lg, cfg.K)
+    np.testing.assert_array_equal(layer.topk_ids.cpu().numpy(), ids)
+    np.testing.assert_allclose(layer.topk_w.cpu().numpy(), gates, rtol=1e-5, atol=1e-7)
+    lay = oracle.layout(ids, cfg.E, cfg.e_begin, cfg.e_end, cfg.cap)
+    for k in ("counts", "offsets", "row_of"):
+        np.testing.assert_array_equal(getattr(layer, k).cpu().numpy(), lay[k])
+    np.testing.assert_array_equal(layer.src_of.cpu().numpy(), lay["src_of"])
+    R = int(lay["offsets"][-1])
+    x = case.x_np()
+    rng = np.random.default_rng(cfg.seed)
+    # dispatch: sampled rows, exact
+    rows = rng.choice(R, size=min(R, 64), replace=False)
+    toks = lay["src_of"][rows] // cfg.K
+    ox, oxs = oracle.dispatch(x[toks], np.arange(len(rows))[:, None], len(rows), cfg.act_dtype)
+    np.testing.assert_array_equal(to_np(layer.xd[torch.as_tensor(rows).cuda()]), ox)
+    if cfg.act_dtype == "fp8":
+        np.testing.assert_array_equal(layer.xd_scales[torch.as_tensor(rows).cuda()].cpu().numpy(), oxs)
+    # expert outputs: all rows of the busiest local expert and of one random one
+    off = lay["offsets"]
+    busiest = int(np.argmax(np.diff(off)))
+    for j in sorted({busiest, int(rng.integers(cfg.E_loc))}):
+        a, b = int(off[j]), int(off[j + 1])
+        if b == a:
+            continue
+        xd_o, xs_o = oracle.dispatch(x[lay["src_of"][a:b] // cfg.K],
+                                     np.arange(b - a)[:, None], b - a, cfg.act_dtype)
+        xv = oracle.numerics.dequantize_fp8_blocks(xd_o, xs_o) if cfg.act_dtype == "fp8" else xd_o
+        y_o = oracle.expert_ffn(xv, *case.oracle_weights(j), cfg.act_dtype, cfg.y_dtype)
+        assert_close(to_np(layer.y[a:b]), y_o, cfg.act_dtype, f"y of local expert {j}")
+    # combined rows of three tokens
+    for t in rng.choice(cfg.T, size=3, replace=False):
+        acc = np.zeros(cfg.H)
+        xv_t, xs_t = oracle.dispatch(x[t:t + 1], np.zeros((1, 1), np.int64), 1, cfg.act_dtype)
+        xv_t = oracle.numerics.dequantize_fp8_blocks(xv_t, xs_t) if cfg.act_dtype == "fp8" else xv_t
+        for k in range(cfg.K):
+            e = int(ids[t, k])
+            if cfg.e_begin <= e < cfg.e_end:
+                yk = oracle.expert_ffn(xv_t, *case.oracle_weights(e - cfg.e_begin),
+                                       cfg.act_dtype, cfg.y_dtype)[0]
+                acc += np.float64(np.float32(gates[t, k])) * yk
+        ref = oracle.numerics.round_act(acc, cfg.out_dtype)
+        assert_close(to_np(layer.out[int(t)]), ref, cfg.act_dtype, f"out[{t}]")
+    del case, layer
+    _free()

@@ -103,7 +103,8 @@ def scaled(cfg: MoEConfig, name: str, *, seg_rows=None, E=None, K=None, H=None, 
               I=cfg.I if I is None else I,
               e_begin=0 if e_begin is None else e_begin,
               e_end=E if e_end is None else e_end,
-              seed=cfg.seed if seed is None else seed)
+              seed=cfg.seed if seed is None else seed,
+              zipf_bias=False)           # the calibrated bias belongs to the named workload only
     return replace(cfg, **kw)
 
 
