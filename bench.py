@@ -76,6 +76,34 @@ def stage_work(cfg, counts_local, tokens_with_local):
     return w, R, touched
 
 
+def measured_traffic(workload: str):
+    """Per-stage HBM bytes (read + write per launch) from the committed
+    rocprofv3 PMC summary of this workload, calibrated against a plain copy
+    kernel.  None when there is no summary or when any listed source file has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    kv, stages = {}, {}
+    for line in open(path):
+        if line.startswith("stage ") and "=" in line:
+            name, vals = line[6:].split("=", 1)
+            r, w = (float(v) for v in vals.split())
+            stages[name.strip()] = r + w
+        elif " = " in line:
+            k, v = line.split(" = ", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256()
+    try:
+        for f in kv["source_files"].split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                sha.update(fh.read())
+    except (KeyError, OSError):
+        return None
+    return stages if sha.hexdigest() == kv.get("source_sha256") else None
+
+
 def roofline_of(work, ms, mfma_peak):
     t = ms / 1e3
     gbs = work["bytes"] / t / 1e9
@@ -228,7 +256,9 @@ def main():
                            "bound": r["bound"]}
     dom = max(stage_rep, key=lambda k: stage_rep[k]["ms"])
     roof = roofline_of(work[dom], stage_rep[dom]["ms"], mfma_peak)
-    roof.update({"kernel": dom, "traffic": None})
+    traffic = measured_traffic(cfg.name)
+    roof.update({"kernel": dom, "traffic": (int(traffic[dom]) if traffic and dom in traffic else None),
+                 "algorithmic_bytes": int(work[dom]["bytes"]), "algorithmic_flops": int(work[dom]["flops"])})
     ffn_ms = stage_rep["ffn_gate_up"]["ms"] + stage_rep["ffn_down"]["ms"]
     ffn_flops = work["ffn_gate_up"]["flops"] + work["ffn_down"]["flops"]
     ffn_bytes = work["ffn_gate_up"]["bytes"] + work["ffn_down"]["bytes"]
@@ -252,10 +282,11 @@ def main():
         "stages": stage_rep,
     }
     if a.copy_calibration_mib:
+        # one elementwise kernel that reads n*4 bytes and writes n*4 bytes
         n = a.copy_calibration_mib * (1 << 20) // 4
         src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
     if not a.no_cpu_baseline:
