@@ -6,15 +6,16 @@
 // post-permute, then combine.  out[t] = sum_k w[t,k] * y[row_of[t,k]] over
 // the local slots, fp32 accumulation in ascending k, one rounding at the end.
 //
-// One block per token; each thread owns 16-byte vectors of the output row
-// and, per vector, issues the loads of all K source rows before summing.
+// One block per (token, slice of 256 8-element vectors of the output row);
+// each thread owns one vector and issues the loads of up to eight source
+// rows before summing them, so a decode-sized batch spreads over the chip.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace moeep {
 namespace {
 
-constexpr int kCombThreads = 128;
+constexpr int kCombThreads = 256;
 constexpr int kMaxKRegs = 8;       // slots whose rows are loaded together
 
 __device__ __forceinline__ void load8(const void* y, int kind, size_t row, int c, int H, float* f) {
@@ -37,42 +38,42 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     int K, int H, int cap, void* __restrict__ out) {
     const int t = blockIdx.x;
     const int nvec = H / 8;
+    const int c = blockIdx.y * kCombThreads + threadIdx.x;
+    if (c >= nvec) return;
     const int32_t* rows = row_of + (size_t)t * K;
     const float* gates = w + (size_t)t * K;
-    for (int c = threadIdx.x; c < nvec; c += kCombThreads) {
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int k0 = 0; k0 < K; k0 += kMaxKRegs) {
-            float v[kMaxKRegs][8];
-            float g[kMaxKRegs];
-            bool use[kMaxKRegs];
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k0 = 0; k0 < K; k0 += kMaxKRegs) {
+        float v[kMaxKRegs][8];
+        float g[kMaxKRegs];
+        bool use[kMaxKRegs];
 #pragma unroll
-            for (int j = 0; j < kMaxKRegs; ++j) {
-                const int k = k0 + j;
-                const int r = k < K ? rows[k] : -1;
-                use[j] = r >= 0 && r < cap;
-                g[j] = use[j] ? gates[k] : 0.0f;
-                if (use[j]) load8(y, KIND == 0 ? 0 : 1, (size_t)r, c, H, v[j]);
-            }
+        for (int j = 0; j < kMaxKRegs; ++j) {
+            const int k = k0 + j;
+            const int r = k < K ? rows[k] : -1;
+            use[j] = r >= 0 && r < cap;
+            g[j] = use[j] ? gates[k] : 0.0f;
+            if (use[j]) load8(y, KIND == 0 ? 0 : 1, (size_t)r, c, H, v[j]);
+        }
 #pragma unroll
-            for (int j = 0; j < kMaxKRegs; ++j) {
-                if (use[j]) {
+        for (int j = 0; j < kMaxKRegs; ++j) {
+            if (use[j]) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[j][i], acc[i]);
-                }
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[j][i], acc[i]);
             }
         }
-        if (KIND == 1) {
-            uint4 o;
-            o.x = pack_bf16x2(acc[0], acc[1]);
-            o.y = pack_bf16x2(acc[2], acc[3]);
-            o.z = pack_bf16x2(acc[4], acc[5]);
-            o.w = pack_bf16x2(acc[6], acc[7]);
-            reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (size_t)t * H)[c] = o;
-        } else {
-            float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H) + 2 * c;
-            p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        }
+    }
+    if (KIND == 1) {
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (size_t)t * H)[c] = o;
+    } else {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H) + 2 * c;
+        p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
 }
 
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 hipError_t launch_combine(const void* y, int kind, const int32_t* row_of, const float* w, int B,
                           int K, int H, void* out, int cap, hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    dim3 grid(B), block(kCombThreads);
+    dim3 grid(B, (H / 8 + kCombThreads - 1) / kCombThreads), block(kCombThreads);
     if (kind == 0)
         hipLaunchKernelGGL(combine_kernel<0>, grid, block, 0, stream, y, row_of, w, K, H, cap, out);
     else if (kind == 1)

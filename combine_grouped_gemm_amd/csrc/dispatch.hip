@@ -6,18 +6,19 @@
 // source ranks (segments), as in the data-parallel attention setting of the
 // same post's "What we have to do".
 //
-// One block per source token: the row is read from HBM once, in 16-byte
-// vectors, and written to each of its local destination rows.  For fp8
-// storage the token is quantised once per 128-element block (16 lanes of
-// one wave cover a block; amax by xor shuffles inside the 16-lane group)
-// and every copy receives the same codes and scale.
+// One block per (source token, slice of 256 16-byte vectors of its row): each
+// thread reads one vector from HBM once and writes it to every local
+// destination row of the token, so a decode-sized batch still spreads over
+// the whole chip.  For fp8 storage the token is quantised once per
+// 128-element block (16 lanes of one wave cover a block; amax by xor shuffles
+// inside the 16-lane group) and every copy receives the same codes and scale.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace moeep {
 namespace {
 
-constexpr int kDispThreads = 128;
+constexpr int kDispThreads = 256;      // one 16-byte source vector per thread
 
 __device__ __forceinline__ const void* token_row(const SegTable& seg, int t, size_t row_bytes) {
     int i = 0;
@@ -30,54 +31,50 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_copy_kernel(
     SegTable seg, size_t row_bytes, const int32_t* __restrict__ row_of, int K, int cap,
     char* __restrict__ xd) {
     const int t = blockIdx.x;
-    const uint4* src = static_cast<const uint4*>(token_row(seg, t, row_bytes));
+    const int c = blockIdx.y * kDispThreads + threadIdx.x;
     const int nvec = (int)(row_bytes / 16);
+    if (c >= nvec) return;
+    const uint4 v = static_cast<const uint4*>(token_row(seg, t, row_bytes))[c];
     const int32_t* rows = row_of + (size_t)t * K;
-    for (int c = threadIdx.x; c < nvec; c += kDispThreads) {
-        const uint4 v = src[c];
-        for (int k = 0; k < K; ++k) {
-            const int r = rows[k];
-            if (r >= 0 && r < cap) reinterpret_cast<uint4*>(xd + (size_t)r * row_bytes)[c] = v;
-        }
+    for (int k = 0; k < K; ++k) {
+        const int r = rows[k];
+        if (r >= 0 && r < cap) reinterpret_cast<uint4*>(xd + (size_t)r * row_bytes)[c] = v;
     }
 }
 
-// bf16 -> fp8 e4m3 with one fp32 scale per 128 elements.
+// bf16 -> fp8 e4m3 with one fp32 scale per 128 elements.  A block's slice
+// starts at a multiple of 256 vectors, so the 16 vectors of a scale block are
+// 16 consecutive lanes of one wave.
 __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
     SegTable seg, int H, const int32_t* __restrict__ row_of, int K, int cap,
     uint8_t* __restrict__ xd, float* __restrict__ xd_scales) {
     const int t = blockIdx.x;
-    const uint4* src = static_cast<const uint4*>(token_row(seg, t, (size_t)H * 2));
+    const int c = blockIdx.y * kDispThreads + threadIdx.x;
     const int nvec = H / 8;                 // 8 bf16 per 16-byte vector
     const int nblk = (H + 127) / 128;
+    const bool ok = c < nvec;
+    const uint4* src = static_cast<const uint4*>(token_row(seg, t, (size_t)H * 2));
+    const uint4 v = ok ? src[c] : make_uint4(0, 0, 0, 0);
+    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+    if (!ok) return;
+    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3_sat(f[i] / s) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3_sat(f[4 + i] / s) << (8 * i);
     const int32_t* rows = row_of + (size_t)t * K;
-    const int iters = (nvec + kDispThreads - 1) / kDispThreads;
-    for (int it = 0; it < iters; ++it) {
-        const int c = it * kDispThreads + threadIdx.x;
-        const bool ok = c < nvec;
-        const uint4 v = ok ? src[c] : make_uint4(0, 0, 0, 0);
-        float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
-        const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3_sat(f[i] / s) << (8 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3_sat(f[4 + i] / s) << (8 * i);
-        if (ok) {
-            const int blk = c / 16;
-            for (int k = 0; k < K; ++k) {
-                const int r = rows[k];
-                if (r < 0 || r >= cap) continue;
-                reinterpret_cast<uint2*>(xd + (size_t)r * H)[c] = make_uint2(lo, hi);
-                if ((c & 15) == 0) xd_scales[(size_t)r * nblk + blk] = s;
-            }
-        }
+    for (int k = 0; k < K; ++k) {
+        const int r = rows[k];
+        if (r < 0 || r >= cap) continue;
+        reinterpret_cast<uint2*>(xd + (size_t)r * H)[c] = make_uint2(lo, hi);
+        if ((c & 15) == 0) xd_scales[(size_t)r * nblk + c / 16] = s;
     }
 }
 
@@ -88,10 +85,13 @@ hipError_t launch_dispatch(const SegTable& seg, int B, int H, int kind, const in
     if (B == 0) return hipSuccess;
     if (kind == 0 || kind == 1) {
         const size_t row_bytes = (size_t)H * (kind == 0 ? 4 : 2);
-        hipLaunchKernelGGL(dispatch_copy_kernel, dim3(B), dim3(kDispThreads), 0, stream, seg,
+        const int nvec = (int)(row_bytes / 16);
+        dim3 grid(B, (nvec + kDispThreads - 1) / kDispThreads);
+        hipLaunchKernelGGL(dispatch_copy_kernel, grid, dim3(kDispThreads), 0, stream, seg,
                            row_bytes, row_of, K, cap, static_cast<char*>(xd));
     } else {
-        hipLaunchKernelGGL(dispatch_fp8_kernel, dim3(B), dim3(kDispThreads), 0, stream, seg, H,
+        dim3 grid(B, (H / 8 + kDispThreads - 1) / kDispThreads);
+        hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kDispThreads), 0, stream, seg, H,
                            row_of, K, cap, static_cast<uint8_t*>(xd), xd_scales);
     }
     return hipGetLastError();

@@ -26,6 +26,7 @@
 // v_mfma_f32_16x16x32_bf16: lane l feeds row (l % 16) with k-chunk (l / 16)
 // of the 32-wide step for both operands and receives rows 4*(l/16)+i,
 // column l % 16 of the 16x16 result.
+#include "gemm_wide.hpp"
 #include "grouped_tiles.hpp"
 
 namespace moeep {
@@ -207,9 +208,19 @@ hipError_t launch_cfg(const FfnArgs& a, hipStream_t stream) {
                              stream, &per_cu);
 }
 
+template <int BK, int WMW, int WNW, bool GATED, int STAGES>
+hipError_t launch_wide(const FfnArgs& a, hipStream_t stream) {
+    static int per_cu = 0;
+    return launch_persistent(wide::grouped_gemm_bf16_wide_kernel<BK, WMW, WNW, GATED, STAGES>,
+                             64 * WMW * WNW, a, stream, &per_cu);
+}
+
 }  // namespace
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, bool gated, hipStream_t stream) {
+    if (a.rows_hint >= 64) {
+        return gated ? launch_wide<64, 2, 4, true, 2>(a, stream) : launch_wide<64, 2, 4, false, 2>(a, stream);
+    }
     if (a.rows_hint < 24) {
         return gated ? launch_cfg<16, 128, 1, 4, true>(a, stream)
                      : launch_cfg<16, 128, 1, 4, false>(a, stream);

@@ -5,7 +5,7 @@
 // prefix sum over local experts of ceil(rows / BM) m-tiles in LDS and maps a
 // linear tile index tau to (expert j, n-tile, m-tile) by binary search, with
 // the m-tile index fastest so that tiles sharing one weight tile are
-// consecutive.  Blocks are renumbered XCD-major (hardware dispatch places
+// consecutive.  An expert's rows are split evenly over its m-tiles.  Blocks are renumbered XCD-major (hardware dispatch places
 // block b on XCD b % 8), so consecutive tile indices run on one XCD and
 // share its L2.
 #pragma once
@@ -81,8 +81,11 @@ __device__ __forceinline__ TileCoord decode_tile(int tau, int n_tiles_n, const i
     t.nt = local / mt_j;
     const int mt = local % mt_j;
     const int r0 = clampi(offsets[lo], 0, cap), r1 = clampi(offsets[lo + 1], 0, cap);
-    t.row0 = r0 + mt * BM;
-    t.nvalid = min(BM, r1 - t.row0);
+    // balanced split: m-tile mt of mt_j takes rows [n*mt/mt_j, n*(mt+1)/mt_j) of the
+    // expert, at most ceil(n/mt_j) <= BM of them
+    const int n = r1 - r0;
+    t.row0 = r0 + (int)(((long long)n * mt) / mt_j);
+    t.nvalid = r0 + (int)(((long long)n * (mt + 1)) / mt_j) - t.row0;
     return t;
 }
 

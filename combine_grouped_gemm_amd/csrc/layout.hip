@@ -11,12 +11,13 @@
 //   1. hist:  one wave per chunk walks it 64 slots at a time; lanes holding
 //             the same expert find each other with a ballot per id bit
 //             (match mask), the lowest such lane adds the group size to an
-//             LDS histogram.  The chunk histogram goes to the workspace.
-//   2. scan:  one block; per expert an exclusive scan over chunks (so chunk
-//             c knows how many earlier slots share its experts), the totals
-//             become `counts`, an exclusive scan over the local experts
-//             gives `offsets`, and every chunk's entry becomes its first
-//             destination row.
+//             LDS histogram.  The chunk histogram goes to the workspace,
+//             expert-major ([E][nchunk]).
+//   2. scan:  one block; a wave per expert scans that expert's chunk counts
+//             (contiguous) with shuffles, so chunk c learns how many earlier
+//             slots share the expert; the totals become `counts`, a block
+//             scan over the local experts gives `offsets`, and every entry
+//             becomes the chunk's first destination row for the expert.
 //   3. rank:  the same walk as 1; a slot's row is its chunk's running base
 //             for the expert plus the number of lower lanes holding the same
 //             expert, which keeps rows of an expert in ascending slot order.
@@ -27,11 +28,11 @@
 namespace moeep {
 namespace {
 
-constexpr int kChunk = 1024;        // slots per chunk (16 wave steps)
+constexpr int kChunk = 256;         // slots per chunk (4 wave steps)
 constexpr int kScanThreads = 1024;  // >= the largest E
 
 struct LayoutWs {
-    int32_t* base;    // [nchunk][E]: chunk histogram, then first row per (chunk, local expert)
+    int32_t* base;    // [E][nchunk]: chunk histogram, then first row per (local expert, chunk)
     int32_t* total;   // 1 int: local rows R
 };
 
@@ -69,8 +70,26 @@ __global__ __launch_bounds__(kWave) void layout_hist_kernel(const int32_t* __res
         __syncthreads();
     }
     __syncthreads();
-    int32_t* out = base + (size_t)blockIdx.x * E;
-    for (int e = lane; e < E; e += kWave) out[e] = s_hist[e];
+    for (int e = lane; e < E; e += kWave) base[(size_t)e * gridDim.x + blockIdx.x] = s_hist[e];
+}
+
+// Exclusive scan of one expert's chunk counts by one wave; returns the total.
+__device__ int wave_scan_row(int32_t* row, int nchunk, int add) {
+    const int lane = threadIdx.x % kWave;
+    int carry = 0;
+    for (int c0 = 0; c0 < nchunk; c0 += kWave) {
+        const int c = c0 + lane;
+        const int v = c < nchunk ? row[c] : 0;
+        int x = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(x, d, kWave);
+            if (lane >= d) x += y;
+        }
+        if (c < nchunk) row[c] = add + carry + x - v;
+        carry += __shfl(x, kWave - 1, kWave);
+    }
+    return carry;
 }
 
 __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
@@ -78,42 +97,38 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ total) {
     __shared__ int32_t s_cnt[kScanThreads];
     __shared__ int32_t s_wave[kScanThreads / kWave];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < E) {
-        for (int c = 0; c < nchunk; ++c) {
-            int32_t* p = base + (size_t)c * E + e;
-            const int v = *p;
-            *p = run;
-            run += v;
-        }
-        counts[e] = run;
-    }
-    // exclusive scan of counts over the local experts, thread j <-> expert e_begin + j
+    constexpr int NW = kScanThreads / kWave;
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
     const int j = threadIdx.x;
     const int E_loc = e_end - e_begin;
     s_cnt[j] = 0;
     __syncthreads();
-    if (e < E && e >= e_begin && e < e_end) s_cnt[e - e_begin] = run;
+    // per expert: exclusive scan over its chunks (relative to the expert's first row)
+    for (int e = wv; e < E; e += NW) {
+        const int tot = wave_scan_row(base + (size_t)e * nchunk, nchunk, 0);
+        if (lane == 0) {
+            counts[e] = tot;
+            if (e >= e_begin && e < e_end) s_cnt[e - e_begin] = tot;
+        }
+    }
     __syncthreads();
-    // inclusive scan within each wave, then across waves
+    // exclusive scan of the local counts, thread j <-> local expert j
     int x = s_cnt[j];
-    const int lane = j % kWave, wv = j / kWave;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
-        int y = __shfl_up(x, d, kWave);
+        const int y = __shfl_up(x, d, kWave);
         if (lane >= d) x += y;
     }
     if (lane == kWave - 1) s_wave[wv] = x;
     __syncthreads();
     if (wv == 0) {
-        int t = (lane < kScanThreads / kWave) ? s_wave[lane] : 0;
+        int t = (lane < NW) ? s_wave[lane] : 0;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
-            int y = __shfl_up(t, d, kWave);
+            const int y = __shfl_up(t, d, kWave);
             if (lane >= d) t += y;
         }
-        if (lane < kScanThreads / kWave) s_wave[lane] = t;
+        if (lane < NW) s_wave[lane] = t;
     }
     __syncthreads();
     const int incl = x + (wv > 0 ? s_wave[wv - 1] : 0);
@@ -124,11 +139,13 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
         *total = incl;
     }
     __syncthreads();
-    s_cnt[j] = excl;               // reuse as the local exclusive offsets
+    s_cnt[j] = excl;               // now the local exclusive offsets
     __syncthreads();
-    if (e < E && e >= e_begin && e < e_end) {
+    // shift every local expert's chunk bases by its offset
+    for (int e = e_begin + wv; e < e_end; e += NW) {
         const int off = s_cnt[e - e_begin];
-        for (int c = 0; c < nchunk; ++c) base[(size_t)c * E + e] += off;
+        int32_t* row = base + (size_t)e * nchunk;
+        for (int c = lane; c < nchunk; c += kWave) row[c] += off;
     }
 }
 
@@ -142,8 +159,7 @@ __global__ __launch_bounds__(kWave) void layout_rank_kernel(
     const int s0 = blockIdx.x * kChunk;
     const int steps = s0 < n_slots ? kChunk : 0;     // an empty input still pads src_of
     if (steps > 0) {
-        const int32_t* my = base + (size_t)blockIdx.x * E + e_begin;
-        for (int j = lane; j < E_loc; j += kWave) s_next[j] = my[j];
+        for (int j = lane; j < E_loc; j += kWave) s_next[j] = base[(size_t)(e_begin + j) * gridDim.x + blockIdx.x];
     }
     __syncthreads();
     const int nbits = id_bits(E);

@@ -70,16 +70,18 @@ def _forced_case(cfg, logits):
     return case
 
 
-@pytest.mark.parametrize("act", ["bf16", "fp8"])
-def test_all_tokens_one_expert_rest_empty(act):
+@pytest.mark.parametrize("act,T", [("bf16", 300), ("bf16", 600), ("fp8", 300)])
+def test_all_tokens_one_expert_rest_empty(act, T):
+    """All rows on one expert (several m-tiles of the 128-row and of the
+    256-row kernels, split evenly), seven experts empty."""
     base = C["dsv3_prefill"] if act == "bf16" else C["gptoss_fp8"]
-    cfg = wl.scaled(base, f"one_expert_{act}", seg_rows=(300,), E=8, K=1, H=256, I=192)
-    lg = np.random.default_rng(0).normal(size=(300, 8)).astype(np.float32)
-    lg[:, 5] += 100.0                      # every token picks expert 5: 300 rows, 7 empty
+    cfg = wl.scaled(base, f"one_expert_{act}_{T}", seg_rows=(T,), E=8, K=1, H=256, I=192)
+    lg = np.random.default_rng(0).normal(size=(T, 8)).astype(np.float32)
+    lg[:, 5] += 100.0                      # every token picks expert 5, 7 experts stay empty
     case = _forced_case(cfg, lg)
     g = gpu_view(run_gpu(case))
     o = case.oracle_layer()
-    assert o["counts"][5] == 300 and (o["counts"] == 0).sum() == 7
+    assert o["counts"][5] == T and (o["counts"] == 0).sum() == 7
     check_exact_stages(g, o, act)
     assert_close(g["y"], o["y"], act, "y")
     assert_close(g["out"], o["out"], act, "out")
