@@ -65,9 +65,9 @@ def lib() -> ctypes.CDLL:
         "moe_layout": ([P, I, I, I, I, I, P, P, P, P, I, P, Z, P], S),
         "moe_dispatch": ([P, P, I, I, I, P, I, P, I, P, I, P], S),
         "moe_ffn_workspace_bytes": ([I, I, I], Z),
-        "moe_ffn_gate_up": ([P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, P], S),
-        "moe_ffn_down": ([P, P, P, I, I, I, I, I, P, P, I, P, I, P], S),
-        "moe_grouped_ffn": ([P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, I, P, Z, P], S),
+        "moe_ffn_gate_up": ([P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, P], S),
+        "moe_ffn_down": ([P, P, P, I, I, I, I, I, P, P, I, P, I, I, P], S),
+        "moe_grouped_ffn": ([P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, I, P, Z, I, P], S),
         "moe_combine": ([P, I, I, P, P, I, I, I, P, I, P], S),
     }
     for name, (args, res) in sig.items():
@@ -208,8 +208,9 @@ def _ffn_shapes(a, w_gate_or_down, gated):
 
 
 def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_up_scales=None,
-                    h=None, h_scales=None, stream=None):
-    """h = silu(Xd Wg^T) * (Xd Wu^T) per local expert -> (cap_rows, I) [+ scales]."""
+                    h=None, h_scales=None, expected_rows=0, stream=None):
+    """h = silu(Xd Wg^T) * (Xd Wu^T) per local expert -> (cap_rows, I) [+ scales].
+    expected_rows: rows a local expert is expected to get (tile-shape hint only)."""
     _dev(xd, "xd", ndim=2)
     _dev(offsets, "offsets", torch.int32, 1)
     _dev(w_gate, "w_gate", xd.dtype, 3)
@@ -223,7 +224,7 @@ def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_
         h_scales = torch.empty((cap, -(-I // FP8_BLOCK)), dtype=torch.float32, device=xd.device)
     _check(lib().moe_ffn_gate_up(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, cap, H, I, act,
                                  _ptr(w_gate), _ptr(w_up), _ptr(w_gate_scales), _ptr(w_up_scales),
-                                 act, _ptr(h), _ptr(h_scales), _stream(stream)))
+                                 act, _ptr(h), _ptr(h_scales), int(expected_rows), _stream(stream)))
     return h, h_scales
 
 
@@ -232,7 +233,7 @@ def _y_dtype_for(act):
 
 
 def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dtype=None,
-                 stream=None):
+                 expected_rows=0, stream=None):
     """y = h Wd^T per local expert -> (cap_rows, H)."""
     _dev(h, "h", ndim=2)
     _dev(offsets, "offsets", torch.int32, 1)
@@ -245,13 +246,13 @@ def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dty
         y = torch.empty((cap, H), dtype=y_dtype, device=h.device)
     _check(lib().moe_ffn_down(_ptr(h), _ptr(h_scales), _ptr(offsets), E_loc, cap, H, I, act,
                               _ptr(w_down), _ptr(w_down_scales), act, _ptr(y), _DT[y.dtype],
-                              _stream(stream)))
+                              int(expected_rows), _stream(stream)))
     return y
 
 
 def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=None,
                     w_up_scales=None, w_down_scales=None, y=None, y_dtype=None, ws=None,
-                    stream=None):
+                    expected_rows=0, stream=None):
     """Both FFN stages with h held in the workspace ``ws``."""
     _dev(xd, "xd", ndim=2)
     _dev(offsets, "offsets", torch.int32, 1)
@@ -270,7 +271,7 @@ def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=
                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
                                  _ptr(w_up_scales), _ptr(w_down_scales), act, _ptr(y),
                                  _DT[y.dtype], _ptr(ws), ws.numel() * ws.element_size(),
-                                 _stream(stream)))
+                                 int(expected_rows), _stream(stream)))
     return y
 
 

@@ -84,7 +84,8 @@ moe_status_t check_y_dtype(moe_dtype_t act_dt, moe_dtype_t y_dt) {
 
 moeep::FfnArgs ffn_args(const void* a, const float* a_scales, const int32_t* offsets, int E_local,
                         int cap_rows, int Kdim, int N, const void* w0, const void* w1,
-                        const float* w0s, const float* w1s, void* out, float* out_scales) {
+                        const float* w0s, const float* w1s, void* out, float* out_scales,
+                        int expected_rows) {
     moeep::FfnArgs f;
     f.a = a;
     f.a_scales = a_scales;
@@ -99,7 +100,7 @@ moeep::FfnArgs ffn_args(const void* a, const float* a_scales, const int32_t* off
     f.w1_scales = w1s;
     f.out = out;
     f.out_scales = out_scales;
-    f.rows_hint = cap_rows / E_local;
+    f.rows_hint = expected_rows > 0 ? expected_rows : cap_rows / E_local;
     return f;
 }
 
@@ -214,7 +215,7 @@ moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32
                              int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
                              const void* w_gate, const void* w_up, const float* w_gate_scales,
                              const float* w_up_scales, moe_dtype_t w_dt, void* h, float* h_scales,
-                             hipStream_t stream) {
+                             int expected_rows, hipStream_t stream) {
     moe_status_t s = check_ffn_common(xd, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
     if (s != MOE_OK) return s;
     REQUIRE(w_gate && w_up && h, "null weight or h pointer");
@@ -222,14 +223,14 @@ moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32
     if (act_dt == MOE_FP8_E4M3)
         REQUIRE(xd_scales && w_gate_scales && w_up_scales && h_scales, "fp8 needs all scale pointers");
     auto f = ffn_args(xd, xd_scales, offsets, E_local, cap_rows, H, I, w_gate, w_up, w_gate_scales,
-                      w_up_scales, h, h_scales);
+                      w_up_scales, h, h_scales, expected_rows);
     return launched(run_ffn(f, act_dt, true, stream), "moe_ffn_gate_up");
 }
 
 moe_status_t moe_ffn_down(const void* h, const float* h_scales, const int32_t* offsets, int E_local,
                           int cap_rows, int H, int I, moe_dtype_t act_dt, const void* w_down,
                           const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
-                          hipStream_t stream) {
+                          int expected_rows, hipStream_t stream) {
     moe_status_t s = check_ffn_common(h, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
     if (s != MOE_OK) return s;
     s = check_y_dtype(act_dt, y_dt);
@@ -238,7 +239,7 @@ moe_status_t moe_ffn_down(const void* h, const float* h_scales, const int32_t* o
     REQUIRE(aligned16(w_down) && aligned16(y), "weights and y must be 16-byte aligned");
     if (act_dt == MOE_FP8_E4M3) REQUIRE(h_scales && w_down_scales, "fp8 needs all scale pointers");
     auto f = ffn_args(h, h_scales, offsets, E_local, cap_rows, I, H, w_down, nullptr, w_down_scales,
-                      nullptr, y, nullptr);
+                      nullptr, y, nullptr, expected_rows);
     return launched(run_ffn(f, act_dt, false, stream), "moe_ffn_down");
 }
 
@@ -247,7 +248,7 @@ moe_status_t moe_grouped_ffn(const void* xd, const float* xd_scales, const int32
                              const void* w_gate, const void* w_up, const void* w_down,
                              const float* w_gate_scales, const float* w_up_scales,
                              const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
-                             void* ws, size_t ws_bytes, hipStream_t stream) {
+                             void* ws, size_t ws_bytes, int expected_rows, hipStream_t stream) {
     moe_status_t s = check_ffn_common(xd, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
     if (s != MOE_OK) return s;
     s = check_y_dtype(act_dt, y_dt);
@@ -261,10 +262,10 @@ moe_status_t moe_grouped_ffn(const void* xd, const float* xd_scales, const int32
     if (act_dt == MOE_FP8_E4M3)
         h_scales = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)cap_rows * I));
     s = moe_ffn_gate_up(xd, xd_scales, offsets, E_local, cap_rows, H, I, act_dt, w_gate, w_up,
-                        w_gate_scales, w_up_scales, w_dt, h, h_scales, stream);
+                        w_gate_scales, w_up_scales, w_dt, h, h_scales, expected_rows, stream);
     if (s != MOE_OK) return s;
     return moe_ffn_down(h, h_scales, offsets, E_local, cap_rows, H, I, act_dt, w_down, w_down_scales,
-                        w_dt, y, y_dt, stream);
+                        w_dt, y, y_dt, expected_rows, stream);
 }
 
 moe_status_t moe_combine(const void* y, moe_dtype_t y_dt, int cap_rows, const int32_t* row_of,

@@ -208,19 +208,21 @@ hipError_t launch_cfg(const FfnArgs& a, hipStream_t stream) {
                              stream, &per_cu);
 }
 
-template <int BK, int WMW, int WNW, bool GATED, int STAGES>
+template <int BM, bool GATED>
 hipError_t launch_wide(const FfnArgs& a, hipStream_t stream) {
     static int per_cu = 0;
-    return launch_persistent(wide::grouped_gemm_bf16_wide_kernel<BK, WMW, WNW, GATED, STAGES>,
-                             64 * WMW * WNW, a, stream, &per_cu);
+    return launch_persistent(wide::grouped_gemm_bf16_wide_kernel<BM, GATED>, 512, a, stream, &per_cu);
 }
 
 }  // namespace
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, bool gated, hipStream_t stream) {
-    if (a.rows_hint >= 64) {
-        return gated ? launch_wide<64, 2, 4, true, 2>(a, stream) : launch_wide<64, 2, 4, false, 2>(a, stream);
-    }
+    // the wide kernels address one expert's weight matrix with 32-bit offsets
+    const bool wide_ok = (unsigned long long)a.N * a.Kdim * 2 < (1ull << 32);
+    if (wide_ok && a.rows_hint >= 192)   // ~256-row experts: one 320-row tile holds nearly all
+        return gated ? launch_wide<320, true>(a, stream) : launch_wide<320, false>(a, stream);
+    if (wide_ok && a.rows_hint >= 64)
+        return gated ? launch_wide<256, true>(a, stream) : launch_wide<256, false>(a, stream);
     if (a.rows_hint < 24) {
         return gated ? launch_cfg<16, 128, 1, 4, true>(a, stream)
                      : launch_cfg<16, 128, 1, 4, false>(a, stream);

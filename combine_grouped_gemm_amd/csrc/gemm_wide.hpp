@@ -1,21 +1,28 @@
 // Wide bf16 grouped GEMM tile for prefill-sized row counts (SwiGLU gate/up
 // or plain down projection), used by ffn_bf16.hip.
 //
-// A tile is 256 rows of one expert (an expert with more rows is split evenly
-// over several tiles) by 256 weight rows (gate/up: 128 gate + 128 up rows of
-// the same output columns, so the SwiGLU epilogue has g and u of a column in
-// one wave).  Almost every expert of a prefill batch fits one m-tile, so each
-// weight tile is streamed from HBM once and reused for all of its rows.
+// A tile is up to BM rows of one expert (an expert with more rows is split
+// evenly over several tiles) by 256 weight rows (gate/up: 128 gate + 128 up
+// rows of the same output columns, so the SwiGLU epilogue has g and u of a
+// column in one wave).  With BM = 320 every expert of a DeepSeek-shaped
+// prefill batch (256 rows on average, a few past 300) fits one m-tile, so
+// each weight tile is streamed from HBM once and feeds all of its rows.
 //
 // Operands go from global memory straight into LDS (global_load_lds_dwordx4:
-// each lane's 16 bytes land at the wave's LDS base + 16 * lane), through a
-// ring of STAGES k-step buffers.  Each buffer is its own __shared__ object
-// and the ring is unrolled so every LDS access names its buffer statically:
-// the compiler can then see that reads of stage s do not alias the loads in
-// flight into the other stages and only waits for stage s (vmcnt counting).
-// The 16-byte chunks of a row are XOR-swizzled so that the 16 rows one MFMA
-// operand read touches fall into distinct LDS banks; the direct loads permute
-// which global chunk each lane fetches to produce that layout.
+// each lane's 16 bytes land at the wave's LDS base + 16 * lane) through two
+// k-step buffers.  Each buffer is its own __shared__ object and the k loop is
+// unrolled by two so every LDS access names its buffer statically: the
+// compiler can then see that reads of one stage do not alias the loads in
+// flight into the other and does not drain the loads before every LDS read.
+// The 16-byte chunks of a row are XOR-swizzled by (row & 7) so the 16 rows
+// one MFMA operand read touches fall into distinct LDS banks; the direct
+// loads permute which global chunk each lane fetches to produce that layout.
+//
+// Measured limits on MI355X that shaped this: the kernel is bound by its load
+// pipeline, not by MFMA or LDS bandwidth; deeper direct-load rings (32-wide
+// k-steps in 4 or 5 stages, or a separate weight ring loaded by dedicated
+// waves) did not help, and a wave with a dozen or more strided direct loads
+// outstanding slows down sharply.
 #pragma once
 
 #include <type_traits>
@@ -25,9 +32,10 @@
 namespace moeep {
 namespace wide {
 
-constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int kObjUint4 = 2048;     // 32 KiB per LDS object
+constexpr int BK = 64;              // bf16 per k-step: 128 bytes per row
+constexpr int CPR = 8;              // 16-byte chunks per row
+constexpr int ROWB = 128;           // bytes per LDS row
 
 template <int N>
 using ic = std::integral_constant<int, N>;
@@ -45,9 +53,9 @@ __device__ __forceinline__ void wait_lgkm0() {
 }
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // those would wait for every load in flight (the direct-to-LDS loads count as
-// LDS stores), which would drain the load ring at every k-step.  The memory
-// clobber keeps the compiler from moving memory accesses across it; the
-// explicit s_waitcnt calls around it order the LDS traffic.
+// LDS stores), which would drain the next stage's loads at every k-step.  The
+// memory clobber keeps the compiler from moving memory accesses across it;
+// the explicit s_waitcnt calls around it order the LDS traffic.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // 16 bytes per lane from global memory straight into LDS at
@@ -60,71 +68,52 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
 #endif
 }
 
-template <int BK, int WMW, int WNW, bool GATED, int S_ = (BK == 32 ? 4 : 2)>
-struct Cfg {
-    static constexpr int NT = 64 * WMW * WNW;
-    static constexpr int NW = WMW * WNW;
-    static constexpr int CPR = BK / 8;                    // 16-byte chunks per row
-    static constexpr int STAGES = S_;                     // BK 32: one 32 KiB object per stage; BK 64: two
-    static constexpr int A_BLOCKS = BM * CPR / 64;         // 1 KiB blocks per stage for A
-    static constexpr int BLOCKS = (BM + BN) * CPR / 64;
-    static constexpr int LPS = BLOCKS / NW;                // direct loads per wave per stage
-    static constexpr int FM = BM / 16 / WMW;               // 16-row fragments per wave
-    static constexpr int WN = BN / WNW;                    // B rows per wave
-    static constexpr int FN = WN / 16;
-    static constexpr int BNO = GATED ? BN / 2 : BN;        // output columns per tile
-    static_assert(BLOCKS % NW == 0 && FN >= 1 && (!GATED || FN % 2 == 0), "tile shape");
-    static_assert(BK == 32 || BK == 64, "k-step");
-    static_assert((BK == 32 && STAGES == 4) || (BK == 64 && STAGES == 2), "ring");
-};
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
 
-__device__ __forceinline__ int swz(int row, int c, int cpr) {
-    return cpr == 8 ? (c ^ (row & 7)) : (c ^ ((row >> 1) & 3));
-}
+// 8 waves laid out 2 (rows) x 4 (weight rows).  A wave owns the interleaved
+// 16-row fragments {wm, wm + 2, ...} (so a short tile still spreads its valid
+// rows over both row-waves) and 64 weight rows.
+template <int BM, bool GATED>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs p) {
+    constexpr int WMW = 2, WNW = 4, NT = 512, NW = 8;
+    constexpr int A_BLOCKS = BM * CPR / 64;          // 1 KiB blocks of a row stage
+    constexpr int BLOCKS = (BM + BN) * CPR / 64;
+    constexpr int LPS = BLOCKS / NW;                 // direct loads per wave per stage
+    constexpr int FM = BM / 16 / WMW;                // 16-row fragments per wave
+    constexpr int WN = BN / WNW;                     // 64 weight rows per wave
+    constexpr int FN = WN / 16;                      // 4
+    constexpr int BNO = GATED ? BN / 2 : BN;         // output columns per tile
+    static_assert(BM % 32 == 0 && BLOCKS % NW == 0 && (!GATED || FN % 2 == 0), "tile shape");
+    // block q = i * NW + wave: whether it is a row block and which weight half it
+    // covers depends only on i, so both are compile-time after unrolling
+    static_assert(A_BLOCKS % NW == 0 && (BN / 16) % NW == 0, "block split");
+    constexpr int A_ITERS = A_BLOCKS / NW;           // i < A_ITERS: row blocks
+    constexpr int G_ITERS = (BN / 16) / NW;          // next G_ITERS: gate (or first) weight half
 
-template <int BK, int WMW, int WNW, bool GATED, int STAGES>
-__global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs p) {
-    using C = Cfg<BK, WMW, WNW, GATED, STAGES>;
-    constexpr int NT = C::NT, CPR = C::CPR, S = C::STAGES, LPS = C::LPS, FM = C::FM, FN = C::FN;
-    constexpr int ROWB = CPR * 16;                         // bytes per LDS row
-
-    __shared__ uint4 o0[kObjUint4];
-    __shared__ uint4 o1[kObjUint4];
-    __shared__ uint4 o2[kObjUint4];
-    __shared__ uint4 o3[kObjUint4];
+    __shared__ uint4 sa0[BM * CPR];
+    __shared__ uint4 sb0[BN * CPR];
+    __shared__ uint4 sa1[BM * CPR];
+    __shared__ uint4 sb1[BN * CPR];
     __shared__ int s_pre[kMaxExperts + 1];
     __shared__ int s_tmp[NT / kWave];
 
-    // stage s: A region and B region (byte pointers)
     auto a_base = [&](auto I) -> char* {
-        constexpr int s = decltype(I)::value;
-        if constexpr (BK == 32) {
-            if constexpr (s == 0) return reinterpret_cast<char*>(o0);
-            else if constexpr (s == 1) return reinterpret_cast<char*>(o1);
-            else if constexpr (s == 2) return reinterpret_cast<char*>(o2);
-            else return reinterpret_cast<char*>(o3);
-        } else {
-            if constexpr (s == 0) return reinterpret_cast<char*>(o0);
-            else return reinterpret_cast<char*>(o2);
-        }
+        if constexpr (decltype(I)::value == 0) return reinterpret_cast<char*>(sa0);
+        else return reinterpret_cast<char*>(sa1);
     };
     auto b_base = [&](auto I) -> char* {
-        constexpr int s = decltype(I)::value;
-        if constexpr (BK == 32) {
-            return a_base(I) + BM * ROWB;
-        } else {
-            if constexpr (s == 0) return reinterpret_cast<char*>(o1);
-            else return reinterpret_cast<char*>(o3);
-        }
+        if constexpr (decltype(I)::value == 0) return reinterpret_cast<char*>(sb0);
+        else return reinterpret_cast<char*>(sb1);
     };
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: keeps LDS bases scalar
     const int wm = wave / WNW, wn = wave % WNW;
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
     const int nk = Kdim / BK;
 
     build_tile_prefix<NT, BM>(p.offsets, p.E_loc, cap, s_pre, s_tmp);
-    const int n_tiles_n = (N + C::BNO - 1) / C::BNO;
+    const int n_tiles_n = (N + BNO - 1) / BNO;
     const int total = n_tiles_n * s_pre[p.E_loc];
     const int G = gridDim.x;
     const int v = xcd_block_order();
@@ -137,45 +126,40 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_bf16_wide_kern
     for (int tau = v; tau < total; tau += G) {
         const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p.E_loc, p.offsets, cap);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
-        const int col0 = tc.nt * C::BNO;
+        const int col0 = tc.nt * BNO;
         const uint16_t* wg = W0 + (size_t)j * N * Kdim;
         const uint16_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
 
-        // per-lane source rows of this wave's direct loads (fixed for the tile)
-        const char* src[LPS];
+        // per-lane source offsets of this wave's direct loads (fixed for the tile),
+        // 32-bit, relative to the row tensor or to the expert's weight matrices;
+        // lanes past the valid rows / columns re-read row 0 so every stage is
+        // exactly LPS vector-memory instructions per wave
+        const char* abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
+        const char* gbase = reinterpret_cast<const char*>(wg);
+        const char* ubase = reinterpret_cast<const char*>(wu);
+        uint32_t off[LPS];
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
-            const int q = i * C::NW + wave;                  // 1 KiB block of the stage
-            const bool is_a = q < C::A_BLOCKS;
-            const int qq = is_a ? q : q - C::A_BLOCKS;
-            const int r = qq * (64 / CPR) + lane / CPR;     // row inside the A or B region
-            const int c = swz(r, lane % CPR, CPR);           // logical chunk this lane fetches
+            const bool is_a = i < A_ITERS;
+            const int r = (is_a ? i * NW : (i - A_ITERS) * NW) * 8 + wave * 8 + lane / 8;
+            const uint32_t c16 = (uint32_t)swz(r, lane % 8) * 16;   // logical chunk this lane fetches
             if (is_a) {
-                src[i] = reinterpret_cast<const char*>(A + (size_t)(row0 + (r < nvalid ? r : 0)) * Kdim) + c * 16;
+                off[i] = (uint32_t)(r < nvalid ? r : 0) * (uint32_t)(Kdim * 2) + c16;
             } else {
-                int col;
-                const uint16_t* w;
-                if (GATED) {
-                    const bool up = r >= BN / 2;
-                    col = col0 + (up ? r - BN / 2 : r);
-                    w = up ? wu : wg;
-                } else {
-                    col = col0 + r;
-                    w = wg;
-                }
-                src[i] = reinterpret_cast<const char*>(w + (size_t)(col < N ? col : 0) * Kdim) + c * 16;
+                const int rr = (GATED && r >= BN / 2) ? r - BN / 2 : r;
+                const int col = col0 + rr;
+                off[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)(Kdim * 2) + c16;
             }
         }
         auto issue = [&](auto I, int kstep) {
 #pragma unroll
             for (int i = 0; i < LPS; ++i) {
-                const int q = i * C::NW + wave;
-                const bool is_a = q < C::A_BLOCKS;
-                char* dst = is_a ? a_base(I) + q * 1024 : b_base(I) + (q - C::A_BLOCKS) * 1024;
-                // issued by every lane, valid or not (invalid lanes re-read a valid row), so
-                // that each stage is exactly LPS vector-memory instructions per wave, which
-                // the vmcnt waits count on
-                lds_dma16(src[i] + (size_t)kstep * BK * 2, dst);
+                const bool is_a = i < A_ITERS;
+                const bool up = GATED && i >= A_ITERS + G_ITERS;
+                const char* b = is_a ? abase : (up ? ubase : gbase);
+                char* dst = is_a ? a_base(I) + (i * NW + wave) * 1024
+                                 : b_base(I) + ((i - A_ITERS) * NW + wave) * 1024;
+                lds_dma16(b + off[i] + (size_t)kstep * BK * 2, dst);
             }
         };
 
@@ -185,40 +169,43 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_bf16_wide_kern
 #pragma unroll
             for (int f = 0; f < FN; ++f) acc[i][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-        auto brow = [&](int f) {
+        auto brow = [&](int f) {      // B-tile row of this lane for n-fragment f
             if (GATED) {
                 const int half = f < FN / 2 ? 0 : BN / 2;
                 const int ff = f < FN / 2 ? f : f - FN / 2;
-                return half + wn * (C::WN / 2) + ff * 16 + (lane & 15);
+                return half + wn * (WN / 2) + ff * 16 + (lane & 15);
             }
-            return wn * C::WN + f * 16 + (lane & 15);
+            return wn * WN + f * 16 + (lane & 15);
         };
-        auto fcol = [&](int f) {
+        auto fcol = [&](int f) {      // output column of fragment f's first lane column
             if (GATED) {
                 const int ff = f < FN / 2 ? f : f - FN / 2;
-                return col0 + wn * (C::WN / 2) + ff * 16;
+                return col0 + wn * (WN / 2) + ff * 16;
             }
-            return col0 + wn * C::WN + f * 16;
+            return col0 + wn * WN + f * 16;
         };
 
+        // v_mfma_f32_16x16x32_bf16: lane l feeds row (l % 16) with k-chunk (l / 16)
+        // of the 32-wide step for both operands and receives rows 4*(l/16)+e,
+        // column l % 16 of the 16x16 result
         auto compute = [&](auto I) {
             const char* ab = a_base(I);
             const char* bb = b_base(I);
 #pragma unroll
-            for (int kk = 0; kk < BK / 32; ++kk) {
+            for (int kk = 0; kk < 2; ++kk) {
                 const int c = kk * 4 + (lane >> 4);
                 bf16x8 bfr[FN];
 #pragma unroll
                 for (int f = 0; f < FN; ++f) {
                     const int r = brow(f);
-                    bfr[f] = *reinterpret_cast<const bf16x8*>(bb + r * ROWB + swz(r, c, CPR) * 16);
+                    bfr[f] = *reinterpret_cast<const bf16x8*>(bb + r * ROWB + swz(r, c) * 16);
                 }
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
                     const int mrow = (wm + WMW * i) * 16;
                     if (mrow < nvalid) {
                         const int r = mrow + (lane & 15);
-                        const bf16x8 afr = *reinterpret_cast<const bf16x8*>(ab + r * ROWB + swz(r, c, CPR) * 16);
+                        const bf16x8 afr = *reinterpret_cast<const bf16x8*>(ab + r * ROWB + swz(r, c) * 16);
 #pragma unroll
                         for (int f = 0; f < FN; ++f)
                             acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[f], acc[i][f], 0, 0, 0);
@@ -227,40 +214,24 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_bf16_wide_kern
             }
         };
 
-        // the previous tile's reads of every stage must be complete before new loads land
+        // the previous tile's reads of both stages must be complete before new loads land
         wait_lgkm0();
         block_barrier();
-        // prologue: stages 0 .. S-2
         issue(ic<0>{}, 0);
-        if constexpr (S > 2) {
-            if (1 < nk) issue(ic<1>{}, 1);
-            if (2 < nk) issue(ic<2>{}, 2);
-        }
 
+        // step k: wait for stage k (nothing else is in flight), then load k+1
+        // into the other buffer while computing k
         auto step = [&](auto I, int k) {
             constexpr int s = decltype(I)::value;
-            // stages issued after k: min(k + S - 2, nk - 1) - k
-            const int after = min(k + S - 2, nk - 1) - k;
-            if constexpr (S == 4) {
-                if (after >= 2) wait_vmcnt<2 * LPS>();
-                else if (after == 1) wait_vmcnt<LPS>();
-                else wait_vmcnt<0>();
-            } else {
-                wait_vmcnt<0>();
-            }
+            wait_vmcnt<0>();
             wait_lgkm0();
             block_barrier();
-            if (k + S - 1 < nk) issue(ic<(s + S - 1) % S>{}, k + S - 1);
+            if (k + 1 < nk) issue(ic<1 - s>{}, k + 1);
             compute(I);
         };
-
-        for (int k = 0; k < nk; k += S) {
+        for (int k = 0; k < nk; k += 2) {
             step(ic<0>{}, k);
             if (k + 1 < nk) step(ic<1>{}, k + 1);
-            if constexpr (S >= 4) {
-                if (k + 2 < nk) step(ic<2>{}, k + 2);
-                if (k + 3 < nk) step(ic<3>{}, k + 3);
-            }
         }
 
         // ---- epilogue
@@ -285,8 +256,6 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_bf16_wide_kern
         }
     }
 }
-
-
 
 }  // namespace wide
 }  // namespace moeep

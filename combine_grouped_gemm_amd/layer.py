@@ -36,6 +36,8 @@ class MoELayer:
         self.E_loc = e_end - e_begin
         self.act_dtype, self.y_dtype, self.out_dtype = act_dtype, y_dtype, out_dtype
         self.cap = self.T * K if cap_rows is None else int(cap_rows)
+        # rows a local expert gets under balanced routing: the FFN tile-shape hint
+        self.expected_rows = max(1, (self.T * K) // E)
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         T, cap = self.T, max(self.cap, 1)
@@ -71,11 +73,11 @@ class MoELayer:
     def gate_up(self, w, stream=None):
         moe_ffn_gate_up(self.xd, self.xd_scales, self.offsets, w["gate"], w["up"],
                         w.get("gate_scale"), w.get("up_scale"), self.h, self.h_scales,
-                        stream=stream)
+                        expected_rows=self.expected_rows, stream=stream)
 
     def down(self, w, stream=None):
         moe_ffn_down(self.h, self.h_scales, self.offsets, w["down"], w.get("down_scale"), self.y,
-                     stream=stream)
+                     expected_rows=self.expected_rows, stream=stream)
 
     def combine(self, stream=None):
         moe_combine(self.y, self.row_of, self.topk_w, self.out, stream=stream)

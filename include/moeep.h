@@ -163,24 +163,27 @@ moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int
  * must hold moe_ffn_workspace_bytes(cap_rows, I, act_dt) bytes.
  * The row counts per expert are read on the device: no host
  * synchronisation, launch sizes depend only on the arguments.
+ * expected_rows is a hint, the rows a local expert is expected to receive
+ * (e.g. B * K / E for balanced routing); it only selects the tile shape and
+ * never changes results.  expected_rows <= 0 means cap_rows / E_local.
  */
 size_t moe_ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt);
 moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32_t* offsets,
                              int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
                              const void* w_gate, const void* w_up,
                              const float* w_gate_scales, const float* w_up_scales, moe_dtype_t w_dt,
-                             void* h, float* h_scales, hipStream_t stream);
+                             void* h, float* h_scales, int expected_rows, hipStream_t stream);
 moe_status_t moe_ffn_down(const void* h, const float* h_scales, const int32_t* offsets,
                           int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
                           const void* w_down, const float* w_down_scales, moe_dtype_t w_dt,
-                          void* y, moe_dtype_t y_dt, hipStream_t stream);
+                          void* y, moe_dtype_t y_dt, int expected_rows, hipStream_t stream);
 moe_status_t moe_grouped_ffn(const void* xd, const float* xd_scales, const int32_t* offsets,
                              int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
                              const void* w_gate, const void* w_up, const void* w_down,
                              const float* w_gate_scales, const float* w_up_scales,
                              const float* w_down_scales, moe_dtype_t w_dt,
                              void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
-                             hipStream_t stream);
+                             int expected_rows, hipStream_t stream);
 
 /*
  * moe_combine -- gate-weighted gather-reduce back to token order.

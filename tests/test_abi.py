@@ -78,16 +78,16 @@ def test_ffn_rejects():
     L = m.lib()
     p = ctypes.c_void_p(4096)
     # bf16 activations with fp8 weights: unsupported
-    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 1, p, p, None, None, 2, p, None, None) == 2
+    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 1, p, p, None, None, 2, p, None, 0, None) == 2
     # I not a multiple of 64
-    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 100, 1, p, p, None, None, 1, p, None, None) == 1
+    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 100, 1, p, p, None, None, 1, p, None, 0, None) == 1
     # fp8 without scales
-    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 2, p, p, None, None, 2, p, None, None) == 1
+    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 2, p, p, None, None, 2, p, None, 0, None) == 1
     # fp8 activations need a bf16 y
-    assert L.moe_ffn_down(p, p, p, 8, 64, 128, 128, 2, p, p, 2, p, 2, None) == 2
+    assert L.moe_ffn_down(p, p, p, 8, 64, 128, 128, 2, p, p, 2, p, 2, 0, None) == 2
     # workspace too small
     assert L.moe_grouped_ffn(p, None, p, 8, 64, 128, 128, 1, p, p, p, None, None, None, 1, p, 1,
-                             p, 16, None) == 1
+                             p, 16, 0, None) == 1
     assert L.moe_ffn_workspace_bytes(64, 128, 2) >= 64 * 128 + 64 * 4
 
 

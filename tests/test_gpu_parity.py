@@ -24,6 +24,7 @@ SMALL = [
     wl.scaled(C["dsv3_decode"], "decode_small", seg_rows=(40,), E=32, K=4, H=512, I=256),
     wl.scaled(C["dsv3_prefill"], "prefill_small", seg_rows=(600,), E=8, K=2, H=384, I=320),
     wl.scaled(C["dsv3_prefill"], "prefill_ntail", seg_rows=(333,), E=6, K=2, H=448, I=192),
+    wl.scaled(C["dsv3_prefill"], "prefill_320_row_tiles", seg_rows=(640,), E=4, K=2, H=256, I=192),
     wl.scaled(C["ep8_share"], "ep_small", seg_rows=(100, 37, 64), E=16, K=3, H=256, I=128,
               e_begin=4, e_end=10),
     wl.scaled(C["gptoss_fp8"], "fp8_small", seg_rows=(300,), E=8, K=2, H=320, I=192),
@@ -137,6 +138,22 @@ def test_capacity_overflow_drops_late_rows():
     ro = layer.row_of.cpu().numpy()
     np.testing.assert_array_equal(ro, np.where(o["row_of"] < cap, o["row_of"], -1))
     np.testing.assert_array_equal(layer.offsets.cpu().numpy(), o["offsets"])
+
+
+def test_fp8_grouped_call_matches_stage_calls():
+    """moe_grouped_ffn carves h and its scales out of the workspace; the result
+    must be bit-identical to the two stage calls with separate buffers."""
+    from combine_grouped_gemm_amd import moe_grouped_ffn
+    cfg = wl.scaled(C["gptoss_fp8"], "fp8_grouped", seg_rows=(256,), E=8, K=2, H=320, I=192)
+    case = Case(cfg)
+    layer = run_gpu(case)
+    w = case.wdict
+    y2 = moe_grouped_ffn(layer.xd, layer.xd_scales, layer.offsets, w["gate"], w["up"], w["down"],
+                         w["gate_scale"], w["up_scale"], w["down_scale"],
+                         expected_rows=layer.expected_rows)
+    torch.cuda.synchronize()
+    R = int(layer.offsets[-1])
+    assert torch.equal(y2[:R], layer.y[:R])
 
 
 def test_deterministic_and_stage_split_matches_grouped_call():
