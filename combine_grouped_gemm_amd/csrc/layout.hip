@@ -13,15 +13,15 @@
 //             (match mask), the lowest such lane adds the group size to an
 //             LDS histogram.  The chunk histogram goes to the workspace,
 //             expert-major ([E][nchunk]).
-//   2. scan:  one block; a wave per expert scans that expert's chunk counts
+//   2. scan:  one wave per expert scans that expert's chunk counts
 //             (contiguous) with shuffles, so chunk c learns how many earlier
-//             slots share the expert; the totals become `counts`, a block
-//             scan over the local experts gives `offsets`, and every entry
-//             becomes the chunk's first destination row for the expert.
-//   3. rank:  the same walk as 1; a slot's row is its chunk's running base
-//             for the expert plus the number of lower lanes holding the same
-//             expert, which keeps rows of an expert in ascending slot order.
-//             Also fills src_of's padding rows with -1.
+//             slots share the expert; the total becomes counts[e].
+//   3. rank:  each chunk's wave scans the local experts' counts into the
+//             offsets (chunk 0 writes `offsets`), adds its per-expert chunk
+//             base, then repeats the walk of 1: a slot's row is the running
+//             base of its expert plus the number of lower lanes holding the
+//             same expert, which keeps rows of an expert in ascending slot
+//             order.  Also fills src_of's padding rows with -1.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -29,11 +29,9 @@ namespace moeep {
 namespace {
 
 constexpr int kChunk = 256;         // slots per chunk (4 wave steps)
-constexpr int kScanThreads = 1024;  // >= the largest E
 
 struct LayoutWs {
-    int32_t* base;    // [E][nchunk]: chunk histogram, then first row per (local expert, chunk)
-    int32_t* total;   // 1 int: local rows R
+    int32_t* base;    // [E][nchunk]: chunk histogram, then each chunk's first rank per expert
 };
 
 __host__ __device__ inline int n_chunks(long long slots) {
@@ -43,7 +41,6 @@ __host__ __device__ inline int n_chunks(long long slots) {
 inline LayoutWs carve(void* ws, int nchunk, int E) {
     LayoutWs w;
     w.base = static_cast<int32_t*>(ws);
-    w.total = w.base + (size_t)nchunk * E;
     return w;
 }
 
@@ -73,9 +70,12 @@ __global__ __launch_bounds__(kWave) void layout_hist_kernel(const int32_t* __res
     for (int e = lane; e < E; e += kWave) base[(size_t)e * gridDim.x + blockIdx.x] = s_hist[e];
 }
 
-// Exclusive scan of one expert's chunk counts by one wave; returns the total.
-__device__ int wave_scan_row(int32_t* row, int nchunk, int add) {
-    const int lane = threadIdx.x % kWave;
+// One wave per expert: exclusive scan of the expert's chunk counts in place
+// (the chunk's first rank among the expert's slots); the total is counts[e].
+__global__ __launch_bounds__(kWave) void layout_scan_kernel(int nchunk, int32_t* __restrict__ base,
+                                                            int32_t* __restrict__ counts) {
+    const int lane = threadIdx.x, e = blockIdx.x;
+    int32_t* row = base + (size_t)e * nchunk;
     int carry = 0;
     for (int c0 = 0; c0 < nchunk; c0 += kWave) {
         const int c = c0 + lane;
@@ -86,81 +86,41 @@ __device__ int wave_scan_row(int32_t* row, int nchunk, int add) {
             const int y = __shfl_up(x, d, kWave);
             if (lane >= d) x += y;
         }
-        if (c < nchunk) row[c] = add + carry + x - v;
+        if (c < nchunk) row[c] = carry + x - v;
         carry += __shfl(x, kWave - 1, kWave);
     }
-    return carry;
-}
-
-__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
-    int nchunk, int E, int e_begin, int e_end, int32_t* __restrict__ base,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ total) {
-    __shared__ int32_t s_cnt[kScanThreads];
-    __shared__ int32_t s_wave[kScanThreads / kWave];
-    constexpr int NW = kScanThreads / kWave;
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-    const int j = threadIdx.x;
-    const int E_loc = e_end - e_begin;
-    s_cnt[j] = 0;
-    __syncthreads();
-    // per expert: exclusive scan over its chunks (relative to the expert's first row)
-    for (int e = wv; e < E; e += NW) {
-        const int tot = wave_scan_row(base + (size_t)e * nchunk, nchunk, 0);
-        if (lane == 0) {
-            counts[e] = tot;
-            if (e >= e_begin && e < e_end) s_cnt[e - e_begin] = tot;
-        }
-    }
-    __syncthreads();
-    // exclusive scan of the local counts, thread j <-> local expert j
-    int x = s_cnt[j];
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
-    }
-    if (lane == kWave - 1) s_wave[wv] = x;
-    __syncthreads();
-    if (wv == 0) {
-        int t = (lane < NW) ? s_wave[lane] : 0;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int y = __shfl_up(t, d, kWave);
-            if (lane >= d) t += y;
-        }
-        if (lane < NW) s_wave[lane] = t;
-    }
-    __syncthreads();
-    const int incl = x + (wv > 0 ? s_wave[wv - 1] : 0);
-    const int excl = incl - s_cnt[j];
-    if (j < E_loc) offsets[j] = excl;
-    if (j == E_loc - 1) {
-        offsets[E_loc] = incl;
-        *total = incl;
-    }
-    __syncthreads();
-    s_cnt[j] = excl;               // now the local exclusive offsets
-    __syncthreads();
-    // shift every local expert's chunk bases by its offset
-    for (int e = e_begin + wv; e < e_end; e += NW) {
-        const int off = s_cnt[e - e_begin];
-        int32_t* row = base + (size_t)e * nchunk;
-        for (int c = lane; c < nchunk; c += kWave) row[c] += off;
-    }
+    if (lane == 0) counts[e] = carry;
 }
 
 __global__ __launch_bounds__(kWave) void layout_rank_kernel(
     const int32_t* __restrict__ ids, int n_slots, int E, int e_begin, int e_end, int cap,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ total,
-    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of) {
+    const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_of, int32_t* __restrict__ src_of) {
     extern __shared__ int32_t s_next[];
     const int lane = threadIdx.x;
     const int E_loc = e_end - e_begin;
     const int s0 = blockIdx.x * kChunk;
     const int steps = s0 < n_slots ? kChunk : 0;     // an empty input still pads src_of
-    if (steps > 0) {
-        for (int j = lane; j < E_loc; j += kWave) s_next[j] = base[(size_t)(e_begin + j) * gridDim.x + blockIdx.x];
+    // local offsets: exclusive scan of counts[e_begin, e_end); plus this chunk's base
+    int carry = 0;
+    for (int j0 = 0; j0 < E_loc; j0 += kWave) {
+        const int j = j0 + lane;
+        const int v = j < E_loc ? counts[e_begin + j] : 0;
+        int x = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(x, d, kWave);
+            if (lane >= d) x += y;
+        }
+        if (j < E_loc) {
+            const int off = carry + x - v;
+            if (blockIdx.x == 0) offsets[j] = off;
+            s_next[j] = off + (steps > 0 ? base[(size_t)(e_begin + j) * gridDim.x + blockIdx.x] : 0);
+        }
+        carry += __shfl(x, kWave - 1, kWave);
     }
+    const int R = carry;                             // local rows
+    if (blockIdx.x == 0 && lane == 0) offsets[E_loc] = R;
     __syncthreads();
     const int nbits = id_bits(E);
     for (int step = 0; step < steps; step += kWave) {
@@ -184,7 +144,6 @@ __global__ __launch_bounds__(kWave) void layout_rank_kernel(
         __syncthreads();
     }
     // padding rows of src_of
-    const int R = *total;
     for (int r = R + blockIdx.x * kWave + lane; r < cap; r += gridDim.x * kWave) src_of[r] = -1;
 }
 
@@ -192,7 +151,7 @@ __global__ __launch_bounds__(kWave) void layout_rank_kernel(
 
 size_t layout_workspace_bytes(int B, int K, int E) {
     const int nchunk = n_chunks((long long)B * K);
-    size_t bytes = ((size_t)nchunk * E + 1) * sizeof(int32_t);
+    size_t bytes = ((size_t)nchunk * E + 1) * sizeof(int32_t);      // never empty
     return (bytes + 255) / 256 * 256;
 }
 
@@ -206,11 +165,10 @@ hipError_t launch_layout(const int32_t* ids, int B, int K, int E, int e_begin, i
         hipLaunchKernelGGL(layout_hist_kernel, dim3(nchunk), dim3(kWave), E * sizeof(int32_t),
                            stream, ids, n_slots, E, w.base);
     }
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, nchunk, E,
-                       e_begin, e_end, w.base, counts, offsets, w.total);
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(E), dim3(kWave), 0, stream, nchunk, w.base, counts);
     hipLaunchKernelGGL(layout_rank_kernel, dim3(nchunk > 0 ? nchunk : 1), dim3(kWave),
                        (e_end - e_begin) * sizeof(int32_t), stream, ids, n_slots, E, e_begin,
-                       e_end, cap, w.base, w.total, row_of, src_of);
+                       e_end, cap, w.base, counts, offsets, row_of, src_of);
     return hipGetLastError();
 }
 
