@@ -9,6 +9,9 @@
 // One block per (token, slice of 256 8-element vectors of the output row);
 // each thread owns one vector and issues the loads of up to eight source
 // rows before summing them, so a decode-sized batch spreads over the chip.
+// Expert outputs are read once, with the non-temporal hint (measured faster
+// than plain loads right after the down GEMM has written them; larger
+// blocks were slower).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -20,12 +23,13 @@ constexpr int kMaxKRegs = 8;       // slots whose rows are loaded together
 
 __device__ __forceinline__ void load8(const void* y, int kind, size_t row, int c, int H, float* f) {
     if (kind == 0) {            // f32: two 16-byte vectors per 8 elements
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + row * H) + 2 * c;
-        float4 a = p[0], b = p[1];
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(y) + row * H) + 2 * c;
+        const uint4 a = load_stream16(p), b = load_stream16(p + 1);
+        f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z);
+        f[3] = __uint_as_float(a.w); f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y);
+        f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
     } else {                    // bf16
-        const uint4 v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row * H)[c];
+        const uint4 v = load_stream16(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row * H) + c);
         f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
         f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
     }

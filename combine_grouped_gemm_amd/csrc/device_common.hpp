@@ -13,6 +13,18 @@ typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
+// Streaming 16-byte loads: the non-temporal hint keeps data read once
+// (weights streamed by a decode GEMM, expert outputs gathered by combine)
+// from displacing reusable lines in L2 and the MALL.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
 // bf16 <-> fp32
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

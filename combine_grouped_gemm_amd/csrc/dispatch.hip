@@ -9,7 +9,8 @@
 // One block per (source token, slice of 256 16-byte vectors of its row): each
 // thread reads one vector from HBM once and writes it to every local
 // destination row of the token, so a decode-sized batch still spreads over
-// the whole chip.  For fp8 storage the token is quantised once per
+// the whole chip.  Plain stores: the non-temporal hint made this kernel
+// slower in the layer's sequence.  For fp8 storage the token is quantised once per
 // 128-element block (16 lanes of one wave cover a block; amax by xor shuffles
 // inside the 16-lane group) and every copy receives the same codes and scale.
 #include "device_common.hpp"

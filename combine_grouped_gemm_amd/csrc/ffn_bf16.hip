@@ -17,7 +17,8 @@
 // row block -- meet in the same L2.
 //
 // Inside a tile: K loop in steps of 64 bf16 (128 bytes per row).  Global
-// 16-byte loads go to registers one step ahead, then to LDS with a XOR
+// 16-byte loads (non-temporal for the weights, which the m-tiles of one
+// expert read close together in tile order) go to registers one step ahead, then to LDS with a XOR
 // swizzle of the 16-byte chunk index by (row & 7), which spreads the 16
 // rows that one MFMA operand read touches over distinct banks.  Waves are
 // laid out WMW x WNW; a wave owns the 16-row fragments {wm, wm + WMW, ...}
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
                         col = col0 + r;
                         src = wg;
                     }
-                    if (col < N) rb[i] = *reinterpret_cast<const uint4*>(src + (size_t)col * Kdim + k0 + c * 8);
+                    if (col < N) rb[i] = load_stream16(src + (size_t)col * Kdim + k0 + c * 8);
                 }
             }
         };

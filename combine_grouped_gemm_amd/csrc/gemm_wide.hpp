@@ -61,10 +61,14 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // 16 bytes per lane from global memory straight into LDS at
 // lds_wave_base + 16 * lane.  The builtin only exists in the device pass; the
 // host pass of a kernel template that names it directly drops the kernel's
-// launch stub, hence the wrapper.
+// launch stub, hence the wrapper.  CPOL is the cache-policy operand: 0 for
+// plain loads, kNonTemporal for data a tile reads once.
+constexpr int kNonTemporal = 2;
+
+template <int CPOL>
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, CPOL);
 #endif
 }
 
@@ -159,7 +163,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
                 const char* b = is_a ? abase : (up ? ubase : gbase);
                 char* dst = is_a ? a_base(I) + (i * NW + wave) * 1024
                                  : b_base(I) + ((i - A_ITERS) * NW + wave) * 1024;
-                lds_dma16(b + off[i] + (size_t)kstep * BK * 2, dst);
+                // weight tiles are read by one or two m-tiles of an expert, all
+                // close together in tile order; the row block is re-read by
+                // every n-tile, so only the weights stream
+                if (is_a)
+                    lds_dma16<0>(b + off[i] + (size_t)kstep * BK * 2, dst);
+                else
+                    lds_dma16<kNonTemporal>(b + off[i] + (size_t)kstep * BK * 2, dst);
             }
         };
 
