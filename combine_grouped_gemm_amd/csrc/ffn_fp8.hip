@@ -3,7 +3,11 @@
 // fp8 quantisation for the grouped GEMM; the block geometry is this
 // library's convention, one scale per 128 contraction elements).
 //
-// Same ragged persistent tile walk as the bf16 kernel.  One k-step is one
+// Two kernels: the wide one (gemm_wide_fp8.hpp: direct global-to-LDS ring,
+// 192-row tiles, scales staged per tile) for expert row counts from a few
+// dozen up and K <= 2944; the register-staged one below for decode-sized
+// row counts or longer K.  The register-staged kernel uses the same ragged
+// persistent tile walk as the bf16 kernel.  One k-step is one
 // 128-wide scale block: v_mfma_f32_16x16x128_f8f6f4 (both operands OCP
 // e4m3) produces the unscaled block product from a zero accumulator, which
 // is folded into the fp32 accumulator as acc += partial * sa[row] * sb[col].
@@ -15,6 +19,7 @@
 // h per row, so the block amax is reduced inside the tile (16 lanes by xor
 // shuffles, then the waves of a row through LDS), s = amax / 448 and the
 // codes are written with the scale.
+#include "gemm_wide_fp8.hpp"
 #include "grouped_tiles.hpp"
 
 namespace moeep {
@@ -290,9 +295,23 @@ hipError_t launch_cfg(const FfnArgs& a, hipStream_t stream) {
                              stream, &per_cu);
 }
 
+template <bool GATED>
+hipError_t launch_wide(const FfnArgs& a, hipStream_t stream) {
+    static int per_cu = 0;
+    return launch_persistent(widefp8::grouped_gemm_fp8_wide_kernel<192, 256, 2, 4, GATED>, 512, a,
+                             stream, &per_cu);
+}
+
 }  // namespace
 
 hipError_t launch_ffn_fp8(const FfnArgs& a, bool gated, hipStream_t stream) {
+    // the wide kernel keeps all of a tile's scale blocks in LDS and addresses an
+    // expert's weight matrix with 32-bit offsets
+    const int nbK = (a.Kdim + 127) / 128;
+    const bool wide_ok = nbK <= widefp8::kMaxKBlocks &&
+                         (unsigned long long)a.N * a.Kdim < (1ull << 32);
+    if (wide_ok && a.rows_hint >= 48)
+        return gated ? launch_wide<true>(a, stream) : launch_wide<false>(a, stream);
     return gated ? launch_cfg<128, 256, 2, 4, true>(a, stream)
                  : launch_cfg<128, 128, 2, 2, false>(a, stream);
 }

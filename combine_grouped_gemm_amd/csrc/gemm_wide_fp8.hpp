@@ -1,0 +1,341 @@
+// Wide fp8 (OCP e4m3) grouped GEMM tile with fp32 1x128 block scales, for
+// expert row counts of a few dozen to ~190 rows (GPT-OSS-shaped prefill),
+// used by ffn_fp8.hip.
+//
+// Same ragged persistent tile walk and direct global-to-LDS two-stage ring as
+// the wide bf16 kernel (every step waits for all loads in flight); one k-step is one 128-byte scale block, so the LDS
+// row geometry (8 swizzled 16-byte chunks per row) is identical.  A tile is
+// up to 192 rows of one expert by 256 weight rows (gate/up: 128 gate + 128
+// up rows of the same output columns, so one tile owns exactly one
+// 128-column block of h and can quantise it in its epilogue).  With 192 rows
+// an expert of a GPT-OSS-shaped batch (128 rows on average) fits one m-tile,
+// so each weight tile is streamed from HBM once.
+//
+// Scales: the tile's row scales and weight-column scales for every k-block
+// are copied to LDS once per tile with 4-byte direct loads (a row range of a
+// scale array is contiguous in global memory).  The MFMA v_mfma_f32_16x16x128_f8f6f4 yields the
+// unscaled block product from a zero accumulator; it is folded in as
+// acc += part * s_row * s_col.  Lane l feeds row (l % 16) with bytes
+// [32*(l/16), 32*(l/16)+32) of the block for both operands.
+//
+// K need not be a multiple of 128 (K = 2880 leaves a 64-byte tail block): in
+// the tail step the direct loads of chunks past K read a 16-byte zero block
+// instead, so both operands are zero there (a garbage fp8 code could be NaN).
+#pragma once
+
+#include "gemm_wide.hpp"
+
+namespace moeep {
+namespace widefp8 {
+
+using wide::ic;
+
+constexpr int CPR = 8;              // 16-byte chunks per 128-byte row step
+constexpr int ROWB = 128;           // bytes per LDS row = fp8 elements per k-step
+constexpr int kMaxKBlocks = 23;     // scale blocks a tile keeps in LDS (K <= 2944)
+
+// source of the tail block's missing chunks
+__device__ __align__(16) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+// 4 bytes per lane from global memory straight into LDS at lds_wave_base + 4 * lane
+__device__ __forceinline__ void lds_dma4(const void* g, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+#endif
+}
+
+// Waves laid out WMW (rows) x WNW (weight rows); a wave owns the interleaved
+// 16-row fragments {wm, wm + WMW, ...} and BN / WNW weight rows.
+template <int BM, int BN, int WMW, int WNW, bool GATED>
+__global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kernel(FfnArgs p) {
+    constexpr int NT = 64 * WMW * WNW, NW = WMW * WNW;
+    constexpr int A_BLOCKS = BM * CPR / 64;          // 1 KiB blocks of a row stage
+    constexpr int B_BLOCKS = BN * CPR / 64;
+    constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;
+    constexpr int LPS = (BLOCKS + NW - 1) / NW;      // direct loads per wave per stage (at most)
+    constexpr int FM = BM / 16 / WMW;
+    constexpr int WN = BN / WNW;
+    constexpr int FN = WN / 16;
+    constexpr int BNO = GATED ? BN / 2 : BN;
+    static_assert(BM % (16 * WMW) == 0 && BN % (16 * WNW) == 0 && (!GATED || (FN % 2 == 0 && BNO == 128)),
+                  "tile shape");
+
+    __shared__ uint4 sa0[BM * CPR];
+    __shared__ uint4 sb0[BN * CPR];
+    __shared__ uint4 sa1[BM * CPR];
+    __shared__ uint4 sb1[BN * CPR];
+    // scales: [tile row][k-block] and, per weight matrix, [weight row][k-block];
+    // a direct load writes 64 floats, so every array has one wave's worth of
+    // slack at its end (lanes past the end must not land in the next array)
+    constexpr int HALF = GATED ? BN / 2 : BN;        // weight rows per scale array
+    constexpr int BS_STRIDE = HALF * kMaxKBlocks + kWave;
+    __shared__ float s_as[kMaxKBlocks * BM + kWave];
+    __shared__ float s_bs[(GATED ? 2 : 1) * BS_STRIDE];
+    __shared__ int s_pre[kMaxExperts + 1];
+    __shared__ int s_tmp[NT / kWave];
+
+    auto a_base = [&](auto I) -> char* {
+        if constexpr (decltype(I)::value == 0) return reinterpret_cast<char*>(sa0);
+        else return reinterpret_cast<char*>(sa1);
+    };
+    auto b_base = [&](auto I) -> char* {
+        if constexpr (decltype(I)::value == 0) return reinterpret_cast<char*>(sb0);
+        else return reinterpret_cast<char*>(sb1);
+    };
+
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / WNW, wn = wave % WNW;
+    const int Kdim = p.Kdim, N = p.N, cap = p.cap;
+    const int nk = (Kdim + ROWB - 1) / ROWB;        // k-steps = scale blocks (<= kMaxKBlocks)
+    const bool k_tail = nk * ROWB != Kdim;          // last block holds 64 bytes
+    const int nbN = (N + 127) / 128;
+
+    build_tile_prefix<NT, BM>(p.offsets, p.E_loc, cap, s_pre, s_tmp);
+    const int n_tiles_n = (N + BNO - 1) / BNO;
+    const int total = n_tiles_n * s_pre[p.E_loc];
+    const int G = gridDim.x;
+    const int v = xcd_block_order();
+
+    const uint8_t* __restrict__ A = static_cast<const uint8_t*>(p.a);
+    const uint8_t* __restrict__ W0 = static_cast<const uint8_t*>(p.w0);
+    const uint8_t* __restrict__ W1 = static_cast<const uint8_t*>(p.w1);
+
+    // logical chunk this lane fetches in every direct load: rows of a 1 KiB
+    // block start at multiples of 8, so (row & 7) = lane / 8
+    const int lchunk = wide::swz(lane / 8, lane % 8);
+
+    for (int tau = v; tau < total; tau += G) {
+        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p.E_loc, p.offsets, cap);
+        const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
+        const int col0 = tc.nt * BNO;
+        const uint8_t* wg = W0 + (size_t)j * N * Kdim;
+        const uint8_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
+        const float* wgs = p.w0_scales + (size_t)j * N * nk;
+        const float* wus = GATED ? p.w1_scales + (size_t)j * N * nk : nullptr;
+
+        // the previous tile's reads of the stages and of the scales are complete
+        wide::wait_lgkm0();
+        wide::block_barrier();
+
+        // ---- this tile's scales -> LDS with 4-byte direct loads; the row range of
+        // a scale array is contiguous in global memory and keeps its [row][k-block]
+        // layout in LDS.  Elements past the valid rows / columns re-read element 0.
+        {
+            const float* asrc = p.a_scales + (size_t)row0 * nk;
+            const int na = nvalid * nk;
+            for (int q0 = wave * kWave; q0 < BM * nk; q0 += NW * kWave) {
+                const int q = q0 + lane;
+                lds_dma4(asrc + (q < na ? q : 0), s_as + q0);
+            }
+            const int nvc = N - col0 < HALF ? N - col0 : HALF;
+            for (int h = 0; h < (GATED ? 2 : 1); ++h) {
+                const float* bsrc = (h ? wus : wgs) + (size_t)col0 * nk;
+                const int nb = nvc * nk;
+                for (int q0 = wave * kWave; q0 < HALF * nk; q0 += NW * kWave) {
+                    const int q = q0 + lane;
+                    lds_dma4(bsrc + (q < nb ? q : 0), s_bs + h * BS_STRIDE + q0);
+                }
+            }
+        }
+
+        // per-lane source offsets (32-bit, relative to the tile's first row or to
+        // the expert's weight matrices).  Wave w loads the 1 KiB blocks w, w + NW, ...
+        // of a stage (8 rows each; row blocks first, then weight blocks); rows /
+        // columns past the valid ones re-read row 0.  Every step waits for all
+        // loads, so waves may issue different numbers of them.
+        const char* abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
+        const char* gbase = reinterpret_cast<const char*>(wg);
+        const char* ubase = reinterpret_cast<const char*>(wu);
+        uint32_t off[LPS];
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int q = i * NW + wave;                 // wave-uniform
+            const uint32_t c16 = (uint32_t)lchunk * 16;
+            if (q < A_BLOCKS) {
+                const int r = q * 8 + lane / 8;
+                off[i] = (uint32_t)(r < nvalid ? r : 0) * (uint32_t)Kdim + c16;
+            } else {
+                const int r = (q - A_BLOCKS) * 8 + lane / 8;
+                const int rr = (GATED && r >= BN / 2) ? r - BN / 2 : r;
+                const int col = col0 + rr;
+                off[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)Kdim + c16;
+            }
+        }
+        auto issue = [&](auto I, int kstep) {
+            const uint32_t kb = (uint32_t)kstep * ROWB;
+            // in a 64-byte tail block, chunks 4..7 come from the zero block
+            const bool zl = k_tail && kstep == nk - 1 && lchunk >= 4;
+#pragma unroll
+            for (int i = 0; i < LPS; ++i) {
+                const int q = i * NW + wave;
+                if (q >= BLOCKS) break;                  // wave-uniform
+                const bool is_a = q < A_BLOCKS;
+                const bool up = GATED && !is_a && (q - A_BLOCKS) * 8 >= BN / 2;
+                const char* b = is_a ? abase : (up ? ubase : gbase);
+                char* dst = is_a ? a_base(I) + q * 1024 : b_base(I) + (q - A_BLOCKS) * 1024;
+                const char* src = zl ? reinterpret_cast<const char*>(kZeroChunk) : b + off[i] + kb;
+                // weight tiles are read by one m-tile of an expert: stream them
+                if (is_a)
+                    wide::lds_dma16<0>(src, dst);
+                else
+                    wide::lds_dma16<wide::kNonTemporal>(src, dst);
+            }
+        };
+
+        floatx4 acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int f = 0; f < FN; ++f) acc[i][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+        auto brow = [&](int f) {      // B-tile row of this lane for n-fragment f
+            if (GATED) {
+                const int half = f < FN / 2 ? 0 : BN / 2;
+                const int ff = f < FN / 2 ? f : f - FN / 2;
+                return half + wn * (WN / 2) + ff * 16 + (lane & 15);
+            }
+            return wn * WN + f * 16 + (lane & 15);
+        };
+        auto fcol = [&](int f) {      // output column of fragment f's first lane column
+            if (GATED) {
+                const int ff = f < FN / 2 ? f : f - FN / 2;
+                return col0 + wn * (WN / 2) + ff * 16;
+            }
+            return col0 + wn * WN + f * 16;
+        };
+
+        const int c0 = 2 * (lane >> 4);                 // first logical chunk this lane feeds
+        auto compute = [&](auto I, int kstep) {
+            const char* ab = a_base(I);
+            const char* bb = b_base(I);
+            intx8 bfr[FN];
+            float bsc[FN];
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const int r = brow(f);
+                const uint4 t0 = *reinterpret_cast<const uint4*>(bb + r * ROWB + wide::swz(r, c0) * 16);
+                const uint4 t1 = *reinterpret_cast<const uint4*>(bb + r * ROWB + wide::swz(r, c0 + 1) * 16);
+                bfr[f] = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
+                               (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
+                bsc[f] = (GATED && f >= FN / 2) ? s_bs[BS_STRIDE + (r - HALF) * nk + kstep]
+                                                : s_bs[r * nk + kstep];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int mrow = (wm + WMW * i) * 16;
+                if (mrow < nvalid) {
+                    const int r = mrow + (lane & 15);
+                    const uint4 t0 = *reinterpret_cast<const uint4*>(ab + r * ROWB + wide::swz(r, c0) * 16);
+                    const uint4 t1 = *reinterpret_cast<const uint4*>(ab + r * ROWB + wide::swz(r, c0 + 1) * 16);
+                    const intx8 afr = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
+                                            (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
+                    // row scales of the four output rows this lane holds
+                    const float* as_row = s_as + (mrow + (lane >> 4) * 4) * nk + kstep;
+                    const float asc[4] = {as_row[0], as_row[nk], as_row[2 * nk], as_row[3 * nk]};
+#pragma unroll
+                    for (int f = 0; f < FN; ++f) {
+                        const floatx4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[e], asc[e] * bsc[f], acc[i][f][e]);
+                    }
+                }
+            }
+        };
+
+        issue(ic<0>{}, 0);
+        // step k: wait for stage k (nothing else is in flight), then load k+1
+        // into the other buffer while computing k
+        auto step = [&](auto I, int k) {
+            constexpr int s = decltype(I)::value;
+            wide::wait_vmcnt<0>();
+            wide::wait_lgkm0();
+            wide::block_barrier();
+            if (k + 1 < nk) issue(ic<1 - s>{}, k + 1);
+            compute(I, k);
+        };
+        for (int k = 0; k < nk; k += 2) {
+            step(ic<0>{}, k);
+            if (k + 1 < nk) step(ic<1>{}, k + 1);
+        }
+
+        // ---- epilogue
+        if constexpr (GATED) {
+            // h = silu(g) * u; the tile's 128 columns are one scale block of h:
+            // row amax over 16 lanes (shuffles) and the 4 column waves, through
+            // the row stage the last k-step did not read (every wave has passed
+            // the barrier after its last read, and no load is in flight)
+            float* s_amax = reinterpret_cast<float*>(((nk - 1) & 1) ? sa0 : sa1);
+            constexpr int FO = FN / 2;
+            float hv[FM][FO][4];
+            float rmax[FM][4];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rmax[i][e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int f = 0; f < FO; ++f)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = fcol(f) + (lane & 15) < N;
+                        const float h = ok ? silu(acc[i][f][e]) * acc[i][f + FO][e] : 0.f;
+                        hv[i][f][e] = h;
+                        rmax[i][e] = fmaxf(rmax[i][e], fabsf(h));
+                    }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float m = rmax[i][e];
+#pragma unroll
+                    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+                    if ((lane & 15) == 0) s_amax[wn * BM + (wm + WMW * i) * 16 + (lane >> 4) * 4 + e] = m;
+                }
+            __syncthreads();
+            uint8_t* Out = static_cast<uint8_t*>(p.out);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int mrow = (wm + WMW * i) * 16;
+                if (mrow >= nvalid) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = mrow + (lane >> 4) * 4 + e;
+                    if (r >= nvalid) continue;
+                    float amax = 0.f;
+#pragma unroll
+                    for (int w = 0; w < WNW; ++w) amax = fmaxf(amax, s_amax[w * BM + r]);
+                    const float s = amax == 0.f ? 1.f : amax / 448.0f;
+#pragma unroll
+                    for (int f = 0; f < FO; ++f) {
+                        const int col = fcol(f) + (lane & 15);
+                        if (col < N) Out[(size_t)(row0 + r) * N + col] = (uint8_t)f32_to_e4m3_sat(hv[i][f][e] / s);
+                    }
+                    if (wn == 0 && (lane & 15) == 0) p.out_scales[(size_t)(row0 + r) * nbN + tc.nt] = s;
+                }
+            }
+        } else {
+            uint16_t* Out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int mrow = (wm + WMW * i) * 16;
+                if (mrow >= nvalid) continue;
+#pragma unroll
+                for (int f = 0; f < FN; ++f) {
+                    const int col = fcol(f) + (lane & 15);
+                    if (col >= N) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = mrow + (lane >> 4) * 4 + e;
+                        if (r < nvalid) Out[(size_t)(row0 + r) * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][f][e]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace widefp8
+}  // namespace moeep
