@@ -139,6 +139,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             }
         }
 
+        const bool w_lines = Kdim % 128 == 0;
         // per-lane source offsets (32-bit, relative to the tile's first row or to
         // the expert's weight matrices).  Wave w loads the 1 KiB blocks w, w + NW, ...
         // of a stage (8 rows each; row blocks first, then weight blocks); rows /
@@ -162,7 +163,10 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 off[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)Kdim + c16;
             }
         }
-        auto issue = [&](auto I, int kstep) {
+        // Weight rows are streamed with the non-temporal hint only when they start
+        // on 128-byte lines: otherwise a k-step's 128 bytes straddle two lines and
+        // the next k-step re-reads the second one, which must still be in L2.
+        auto issue_p = [&](auto I, int kstep, auto WPOL) {
             const uint32_t kb = (uint32_t)kstep * ROWB;
             // in a 64-byte tail block, chunks 4..7 come from the zero block
             const bool zl = k_tail && kstep == nk - 1 && lchunk >= 4;
@@ -175,12 +179,15 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 const char* b = is_a ? abase : (up ? ubase : gbase);
                 char* dst = is_a ? a_base(I) + q * 1024 : b_base(I) + (q - A_BLOCKS) * 1024;
                 const char* src = zl ? reinterpret_cast<const char*>(kZeroChunk) : b + off[i] + kb;
-                // weight tiles are read by one m-tile of an expert: stream them
                 if (is_a)
                     wide::lds_dma16<0>(src, dst);
                 else
-                    wide::lds_dma16<wide::kNonTemporal>(src, dst);
+                    wide::lds_dma16<decltype(WPOL)::value>(src, dst);
             }
+        };
+        auto issue = [&](auto I, int kstep) {
+            if (w_lines) issue_p(I, kstep, ic<wide::kNonTemporal>{});
+            else issue_p(I, kstep, ic<0>{});
         };
 
         floatx4 acc[FM][FN];
