@@ -104,6 +104,23 @@ def measured_traffic(workload: str):
     return stages if sha.hexdigest() == kv.get("source_sha256") else None
 
 
+def measured_copy_gbs(dev, mib=1024, reps=5):
+    """Achievable-bandwidth reference: GB/s (read + write) of torch's device
+    copy of `mib` MiB, timed with events."""
+    src = torch.empty(mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * src.numel() * 4 * reps / (t0.elapsed_time(t1) / 1e3) / 1e9
+    del src, dst
+    return gbs
+
+
 def roofline_of(work, ms, mfma_peak):
     t = ms / 1e3
     gbs = work["bytes"] / t / 1e9
@@ -218,6 +235,7 @@ def main():
     local = (ids >= cfg.e_begin) & (ids < cfg.e_end)
     work, R, touched = stage_work(cfg, counts_local, int(local.any(axis=1).sum()))
 
+    copy_gbs = measured_copy_gbs(dev)
     stream = torch.cuda.current_stream()
     for _ in range(a.warmup):
         for _, run in stages:
@@ -246,12 +264,14 @@ def main():
     for name, _ in stages:
         ms = float(np.mean(per[name]))
         r = roofline_of(work[name], ms, mfma_peak)
-        stage_rep[name] = {"ms": round(ms, 4), "ms_p10": round(float(np.percentile(per[name], 10)), 4),
+        stage_rep[name] = {"ms": round(ms, 4), "ms_median": round(float(np.median(per[name])), 4),
+                           "ms_p10": round(float(np.percentile(per[name], 10)), 4),
                            "ms_p90": round(float(np.percentile(per[name], 90)), 4),
                            "GB_s": round(work[name]["bytes"] / (ms / 1e3) / 1e9, 1),
                            "TFLOP_s": round(work[name]["flops"] / (ms / 1e3) / 1e12, 2),
                            "hbm_frac": round(work[name]["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                            "mfma_frac": round(work[name]["flops"] / (ms / 1e3) / 1e12 / mfma_peak, 4),
+                           "copy_frac": round(work[name]["bytes"] / (ms / 1e3) / 1e9 / copy_gbs, 4),
                            "bytes": int(work[name]["bytes"]), "flops": int(work[name]["flops"]),
                            "bound": r["bound"]}
     dom = max(stage_rep, key=lambda k: stage_rep[k]["ms"])
@@ -280,6 +300,9 @@ def main():
                         "GB_s": round(ffn_bytes / (ffn_ms / 1e3) / 1e9, 1),
                         "hbm_frac": round(ffn_bytes / (ffn_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "stages": stage_rep,
+        "hbm_reference": {"copy_GB_s": round(copy_gbs, 1),
+                          "note": "device-to-device copy of 1 GiB measured in this run (read + write bytes); "
+                                  "copy_frac of a stage = its algorithmic GB/s / this"},
     }
     if a.copy_calibration_mib:
         # one elementwise kernel that reads n*4 bytes and writes n*4 bytes
