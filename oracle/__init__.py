@@ -19,6 +19,9 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   route          pinned: worked rows, closed-form two-way gates, full softmax
                  at K = E, brute-force top-K over {-1,0,1}^E.
   layout         pinned: brute-force construction, sum of counts, bijection.
+  layout_masked  pinned: agrees with the contiguous layout (a different
+                 construction) shifted to fixed row blocks; overflow keeps the
+                 first cap_e slots of an expert in (t, k) order.
   dispatch/combine pinned: identity-expert round trip returns x * sum(gates).
   expert_ffn     pinned: dense SwiGLU via torch CPU, pure-Python brute force.
   numerics       pinned: exhaustive bf16 / e4m3 casts against torch.
@@ -26,8 +29,8 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   both sides implement); its properties are checked.
 """
 from . import numerics
-from .moe import (route, layout, dispatch, silu, expert_ffn, grouped_ffn,
-                  combine, layer)
+from .moe import (route, layout, layout_masked, dispatch, silu, expert_ffn, grouped_ffn,
+                  grouped_ffn_masked, combine, layer)
 
-__all__ = ["numerics", "route", "layout", "dispatch", "silu", "expert_ffn",
-           "grouped_ffn", "combine", "layer"]
+__all__ = ["numerics", "route", "layout", "layout_masked", "dispatch", "silu", "expert_ffn",
+           "grouped_ffn", "grouped_ffn_masked", "combine", "layer"]

@@ -103,6 +103,45 @@ def layout(ids, E: int, e_begin: int, e_end: int, cap: int):
             "row_of": row_of.reshape(B, K), "src_of": src_of}
 
 
+def layout_masked(ids, E: int, e_begin: int, e_end: int, cap_e: int):
+    """Fixed-capacity ("masked") layout of the routed slots.
+
+    SGLang "Expert Parallelism", MoE-runner backend table: the grouped GEMM
+    takes a contiguous layout for prefill and a masked layout for decode; the
+    same page's dispatch paragraph pairs the low-latency (decode) mode with
+    CUDA-graph compatibility.  The page gives no further detail; the reading
+    used here: local expert j owns the fixed row block [j*cap_e, (j+1)*cap_e)
+    and a count m[j] of valid rows (the mask), so every size is static.
+
+    counts[e]   number of (t, k) with ids[t, k] == e, over all E experts.
+    m[j]        valid rows of local expert j = min(counts[e_begin + j], cap_e).
+    row_of[t,k] j*cap_e + (rank of (t, k) among the slots routed to local
+                expert j, in (t, k) order), or -1 when the expert is not local
+                or the rank is >= cap_e (the slot is dropped).
+    src_of[r]   slot index t*K + k held by row r, -1 for unused rows.
+    """
+    ids = np.asarray(ids)
+    B, K = ids.shape
+    E_loc = e_end - e_begin
+    counts = np.zeros(E, dtype=np.int32)
+    m = np.zeros(E_loc, dtype=np.int32)
+    row_of = np.full((B, K), -1, dtype=np.int32)
+    src_of = np.full(E_loc * cap_e, -1, dtype=np.int32)
+    for t in range(B):                     # slots in (t, k) order
+        for k in range(K):
+            e = int(ids[t, k])
+            if not 0 <= e < E:
+                continue
+            rank = int(counts[e])
+            counts[e] += 1
+            if e_begin <= e < e_end and rank < cap_e:
+                j = e - e_begin
+                row_of[t, k] = j * cap_e + rank
+                src_of[j * cap_e + rank] = t * K + k
+                m[j] += 1
+    return {"counts": counts, "m": m, "row_of": row_of, "src_of": src_of}
+
+
 # ----------------------------------------------------------------------------
 # dispatch
 # ----------------------------------------------------------------------------
@@ -180,6 +219,18 @@ def grouped_ffn(xd, offsets, weights_of, h_dtype: str, y_dtype: str):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
             y[a:b] = expert_ffn(xd[a:b], *weights_of(e), h_dtype, y_dtype)
+    return y
+
+
+def grouped_ffn_masked(xd, m, cap_e: int, weights_of, h_dtype: str, y_dtype: str):
+    """The grouped FFN over a masked layout: local expert j runs on rows
+    [j*cap_e, j*cap_e + m[j]); the other rows of y stay zero."""
+    xd = np.asarray(xd, dtype=np.float64)
+    y = np.zeros_like(xd)
+    for j, n in enumerate(np.asarray(m)):
+        a = j * cap_e
+        if n > 0:
+            y[a:a + n] = expert_ffn(xd[a:a + n], *weights_of(j), h_dtype, y_dtype)
     return y
 
 

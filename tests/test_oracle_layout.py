@@ -139,3 +139,73 @@ def test_fp8_dispatch_copies_identical_codes():
         # e4m3 keeps 3 fraction bits: relative error <= 2^-4 of the block max
         amax = np.maximum(np.abs(x[t, :128]).max(), 1e-30)
         assert np.max(np.abs(deq[:128] - x[t, :128])) <= amax / 448 * 16 * 1.0001
+
+
+# ---------------------------------------------------------------------------
+# masked (fixed-capacity) layout
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,K,E,e_begin,e_end,seed", [
+    (1, 1, 1, 0, 1, 0), (9, 3, 7, 2, 5, 2), (33, 8, 32, 0, 4, 3), (64, 2, 16, 0, 16, 5),
+    (128, 8, 256, 0, 256, 6)])
+def test_masked_layout_is_contiguous_layout_in_fixed_blocks(B, K, E, e_begin, e_end, seed):
+    """With room for every row, the masked layout is the contiguous one with
+    expert j's rows moved from offsets[j] to j*cap_e (the contiguous oracle
+    builds its permutation by a stable sort, the masked one by running ranks)."""
+    rng = np.random.default_rng(seed)
+    ids, _ = oracle.route(rng.standard_normal((B, E)).astype(np.float32), K)
+    lay = oracle.layout(ids, E, e_begin, e_end, B * K)
+    cap_e = int(max(lay["counts"].max(), 1))
+    mk = oracle.layout_masked(ids, E, e_begin, e_end, cap_e)
+    np.testing.assert_array_equal(mk["counts"], lay["counts"])
+    np.testing.assert_array_equal(mk["m"], np.diff(lay["offsets"]))
+    off = lay["offsets"]
+    for t in range(B):
+        for k in range(K):
+            r = lay["row_of"][t, k]
+            if r < 0:
+                assert mk["row_of"][t, k] == -1
+                continue
+            j = int(np.searchsorted(off, r, side="right") - 1)
+            assert mk["row_of"][t, k] == j * cap_e + (r - off[j])
+    # src_of inverts row_of on the valid rows; the rest are -1
+    valid = mk["src_of"] >= 0
+    assert valid.sum() == off[-1]
+    rows = np.nonzero(valid)[0]
+    flat = mk["row_of"].reshape(-1)
+    np.testing.assert_array_equal(flat[mk["src_of"][rows]], rows)
+
+
+def test_masked_layout_overflow_keeps_first_slots():
+    """An expert with more slots than cap_e keeps its first cap_e slots in
+    (t, k) order; the rest are dropped (row_of = -1) but still counted."""
+    ids = np.array([[0, 1], [0, 2], [1, 0], [0, 3], [2, 0]], dtype=np.int32)
+    mk = oracle.layout_masked(ids, 4, 0, 4, 2)
+    np.testing.assert_array_equal(mk["counts"], [5, 2, 2, 1])
+    np.testing.assert_array_equal(mk["m"], [2, 2, 2, 1])
+    # expert 0 slots in order: (0,0) (1,0) (2,1) (3,0) (4,1) -> first two kept
+    assert mk["row_of"][0, 0] == 0 and mk["row_of"][1, 0] == 1
+    assert mk["row_of"][2, 1] == -1 and mk["row_of"][3, 0] == -1 and mk["row_of"][4, 1] == -1
+    assert mk["row_of"][0, 1] == 2 and mk["row_of"][2, 0] == 3      # expert 1 block starts at 2
+    assert mk["row_of"][1, 1] == 4 and mk["row_of"][4, 0] == 5      # expert 2
+    assert mk["row_of"][3, 1] == 6                                   # expert 3
+    np.testing.assert_array_equal(mk["src_of"], [0, 2, 1, 4, 3, 8, 7, -1])
+
+
+def test_masked_grouped_ffn_matches_contiguous():
+    """The masked grouped FFN on the masked buffer equals the contiguous one
+    on the contiguous buffer, row for row."""
+    rng = np.random.default_rng(11)
+    B, K, E, H, I = 12, 2, 4, 8, 6
+    ids, _ = oracle.route(rng.standard_normal((B, E)).astype(np.float32), K)
+    x = rng.standard_normal((B, H))
+    W = [tuple(rng.standard_normal(s) for s in ((I, H), (I, H), (H, I))) for _ in range(E)]
+    lay = oracle.layout(ids, E, 0, E, B * K)
+    cap_e = int(lay["counts"].max()) + 1
+    mk = oracle.layout_masked(ids, E, 0, E, cap_e)
+    xd_c, _ = oracle.dispatch(x, lay["row_of"], B * K, "f32")
+    xd_m, _ = oracle.dispatch(x, mk["row_of"], E * cap_e, "f32")
+    y_c = oracle.grouped_ffn(xd_c, lay["offsets"], lambda e: W[e], "f32", "f32")
+    y_m = oracle.grouped_ffn_masked(xd_m, mk["m"], cap_e, lambda e: W[e], "f32", "f32")
+    flat_c, flat_m = lay["row_of"].reshape(-1), mk["row_of"].reshape(-1)
+    for s in range(B * K):
+        np.testing.assert_array_equal(y_m[flat_m[s]], y_c[flat_c[s]])
