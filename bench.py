@@ -45,6 +45,12 @@ def parse():
                     help="target CPU seconds for the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for counter calibration)")
+    ap.add_argument("--layout", default="contiguous", choices=["contiguous", "masked"],
+                    help="expert row layout: contiguous (offsets) or masked (fixed block per expert)")
+    ap.add_argument("--cap-per-expert", type=int, default=0,
+                    help="masked layout: rows per expert block (default T, nothing dropped)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step as a HIP graph and time its replays")
     return ap.parse_args()
 
 
@@ -119,6 +125,29 @@ def measured_copy_gbs(dev, mib=1024, reps=5):
     gbs = 2 * src.numel() * 4 * reps / (t0.elapsed_time(t1) / 1e3) / 1e9
     del src, dst
     return gbs
+
+
+def graph_replay(layer, x, logits, wdict, steps, warmup):
+    """Capture one step (the six library calls) as a HIP graph and time
+    `steps` back-to-back replays; returns ms per replayed step."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x, logits, wdict)
+        with torch.cuda.graph(g, stream=s):
+            layer.forward(x, logits, wdict)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(layer.T / (ms / 1e3), 1),
+            "steps": steps}
 
 
 def roofline_of(work, ms, mfma_peak):
@@ -218,7 +247,8 @@ def main():
     if cfg.w_dtype == "fp8":
         wdict.update(gate_scale=W.gate_scale, up_scale=W.up_scale, down_scale=W.down_scale)
     layer = m.MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end,
-                       cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=dev)
+                       cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=dev, layout=a.layout,
+                       cap_per_expert=(a.cap_per_expert or None))
     stages = layer.stages(x, logits, wdict)
 
     # parity gate before timing: routing and layout must equal the oracle's
@@ -227,8 +257,10 @@ def main():
     import oracle
     ids, _ = oracle.route(logits_cpu.numpy(), cfg.K)
     lay = oracle.layout(ids, cfg.E, cfg.e_begin, cfg.e_end, cfg.cap)
+    ref_row_of = (oracle.layout_masked(ids, cfg.E, cfg.e_begin, cfg.e_end, layer.cap_e)["row_of"]
+                  if layer.masked else lay["row_of"])
     if not (np.array_equal(layer.topk_ids.cpu().numpy(), ids)
-            and np.array_equal(layer.row_of.cpu().numpy(), lay["row_of"])):
+            and np.array_equal(layer.row_of.cpu().numpy(), ref_row_of)):
         print(json.dumps({"error": "parity gate failed: routing/layout differ from the oracle"}))
         sys.exit(1)
     counts_local = lay["counts"][cfg.e_begin:cfg.e_end]
@@ -304,6 +336,10 @@ def main():
                           "note": "device-to-device copy of 1 GiB measured in this run (read + write bytes); "
                                   "copy_frac of a stage = its algorithmic GB/s / this"},
     }
+    if a.layout == "masked":
+        res["config"]["layout"] = {"kind": "masked", "cap_per_expert": layer.cap_e}
+    if a.graph:
+        res["graph_replay"] = graph_replay(layer, x, logits, wdict, a.steps, a.warmup)
     if a.copy_calibration_mib:
         # one elementwise kernel that reads n*4 bytes and writes n*4 bytes
         n = a.copy_calibration_mib * (1 << 20) // 4

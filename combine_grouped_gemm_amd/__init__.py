@@ -19,7 +19,8 @@ import torch
 __all__ = ["MoeError", "lib", "library_path", "moe_version", "moe_route",
            "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
            "moe_ffn_workspace_bytes", "moe_ffn_gate_up", "moe_ffn_down",
-           "moe_grouped_ffn", "moe_combine", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
+           "moe_grouped_ffn", "moe_combine", "moe_layout_masked", "moe_ffn_gate_up_masked",
+           "moe_ffn_down_masked", "moe_grouped_ffn_masked", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
            "MoELayer"]
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
@@ -69,7 +70,12 @@ def lib() -> ctypes.CDLL:
         "moe_ffn_down": ([P, P, P, I, I, I, I, I, P, P, I, P, I, I, P], S),
         "moe_grouped_ffn": ([P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, I, P, Z, I, P], S),
         "moe_combine": ([P, I, I, P, P, I, I, I, P, I, P], S),
+        "moe_layout_masked": ([P, I, I, I, I, I, P, P, P, P, I, P, Z, P], S),
     }
+    # the masked FFN calls take (m, E_local, cap_per_expert) where the others take
+    # (offsets, E_local, cap_rows): same argument types
+    for name in ("moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn"):
+        sig[name + "_masked"] = sig[name]
     for name, (args, res) in sig.items():
         f = getattr(L, name)
         f.argtypes, f.restype = args, res
@@ -162,6 +168,31 @@ def moe_layout(topk_ids, E: int, e_begin: int, e_end: int, cap_rows: int, counts
     return {"counts": counts, "offsets": offsets, "row_of": row_of, "src_of": src_of}
 
 
+def moe_layout_masked(topk_ids, E: int, e_begin: int, e_end: int, cap_per_expert: int, counts=None,
+                      m=None, row_of=None, src_of=None, ws=None, stream=None) -> dict:
+    """Fixed-capacity layout: counts (E), m (E_loc), row_of (B, K),
+    src_of (E_loc * cap_per_expert), all int32."""
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    B, K = topk_ids.shape
+    dev = topk_ids.device
+    E_loc = e_end - e_begin
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    m = torch.empty(max(E_loc, 1), dtype=torch.int32, device=dev) if m is None else m
+    row_of = torch.empty((B, K), dtype=torch.int32, device=dev) if row_of is None else row_of
+    if src_of is None:
+        src_of = torch.empty(max(E_loc * cap_per_expert, 1), dtype=torch.int32, device=dev)
+    need = moe_layout_workspace_bytes(B, K, E)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    for n, t in (("counts", counts), ("m", m), ("row_of", row_of), ("src_of", src_of)):
+        _dev(t, n, torch.int32)
+    _dev(ws, "ws")
+    _check(lib().moe_layout_masked(_ptr(topk_ids), B, K, E, e_begin, e_end, _ptr(counts), _ptr(m),
+                                   _ptr(row_of), _ptr(src_of), cap_per_expert, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
+    return {"counts": counts, "m": m, "row_of": row_of, "src_of": src_of}
+
+
 def moe_dispatch(seg_x, row_of, cap_rows: int, xd_dtype=None, xd=None, xd_scales=None,
                  stream=None):
     """Scatter the token rows of the segments into xd (cap_rows, H); fp8
@@ -207,24 +238,39 @@ def _ffn_shapes(a, w_gate_or_down, gated):
     return E_loc, H, I
 
 
+def _rows_arg(rows, cap_per_expert, E_loc, n_rows):
+    """(pointer tensor, third int argument) of the row description: offsets
+    (E_loc+1) of the contiguous layout, or m (E_loc) of the masked one."""
+    _dev(rows, "offsets" if cap_per_expert is None else "m", torch.int32, 1)
+    if cap_per_expert is None:
+        return n_rows
+    if n_rows != E_loc * cap_per_expert:
+        raise ValueError(f"masked layout needs E_loc * cap_per_expert = {E_loc * cap_per_expert} rows, "
+                         f"got {n_rows}")
+    return int(cap_per_expert)
+
+
 def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_up_scales=None,
-                    h=None, h_scales=None, expected_rows=0, stream=None):
+                    h=None, h_scales=None, expected_rows=0, stream=None, cap_per_expert=None):
     """h = silu(Xd Wg^T) * (Xd Wu^T) per local expert -> (cap_rows, I) [+ scales].
-    expected_rows: rows a local expert is expected to get (tile-shape hint only)."""
+    expected_rows: rows a local expert is expected to get (tile-shape hint only).
+    With cap_per_expert given, ``offsets`` is the masked layout's m and the call
+    is moe_ffn_gate_up_masked."""
     _dev(xd, "xd", ndim=2)
-    _dev(offsets, "offsets", torch.int32, 1)
     _dev(w_gate, "w_gate", xd.dtype, 3)
     _dev(w_up, "w_up", xd.dtype, 3)
     E_loc, H, I = _ffn_shapes(xd, w_gate, True)
     cap = xd.shape[0]
+    third = _rows_arg(offsets, cap_per_expert, E_loc, cap)
     act = _DT[xd.dtype]
     if h is None:
         h = torch.empty((cap, I), dtype=xd.dtype, device=xd.device)
     if act == MOE_FP8_E4M3 and h_scales is None:
         h_scales = torch.empty((cap, -(-I // FP8_BLOCK)), dtype=torch.float32, device=xd.device)
-    _check(lib().moe_ffn_gate_up(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, cap, H, I, act,
-                                 _ptr(w_gate), _ptr(w_up), _ptr(w_gate_scales), _ptr(w_up_scales),
-                                 act, _ptr(h), _ptr(h_scales), int(expected_rows), _stream(stream)))
+    fn = lib().moe_ffn_gate_up if cap_per_expert is None else lib().moe_ffn_gate_up_masked
+    _check(fn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, third, H, I, act,
+              _ptr(w_gate), _ptr(w_up), _ptr(w_gate_scales), _ptr(w_up_scales),
+              act, _ptr(h), _ptr(h_scales), int(expected_rows), _stream(stream)))
     return h, h_scales
 
 
@@ -233,33 +279,36 @@ def _y_dtype_for(act):
 
 
 def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dtype=None,
-                 expected_rows=0, stream=None):
-    """y = h Wd^T per local expert -> (cap_rows, H)."""
+                 expected_rows=0, stream=None, cap_per_expert=None):
+    """y = h Wd^T per local expert -> (cap_rows, H).  cap_per_expert: as in
+    moe_ffn_gate_up (moe_ffn_down_masked)."""
     _dev(h, "h", ndim=2)
-    _dev(offsets, "offsets", torch.int32, 1)
     _dev(w_down, "w_down", h.dtype, 3)
     E_loc, H, I = _ffn_shapes(h, w_down, False)
     cap = h.shape[0]
+    third = _rows_arg(offsets, cap_per_expert, E_loc, cap)
     act = _DT[h.dtype]
     y_dtype = _y_dtype_for(act) if y_dtype is None else y_dtype
     if y is None:
         y = torch.empty((cap, H), dtype=y_dtype, device=h.device)
-    _check(lib().moe_ffn_down(_ptr(h), _ptr(h_scales), _ptr(offsets), E_loc, cap, H, I, act,
-                              _ptr(w_down), _ptr(w_down_scales), act, _ptr(y), _DT[y.dtype],
-                              int(expected_rows), _stream(stream)))
+    fn = lib().moe_ffn_down if cap_per_expert is None else lib().moe_ffn_down_masked
+    _check(fn(_ptr(h), _ptr(h_scales), _ptr(offsets), E_loc, third, H, I, act,
+              _ptr(w_down), _ptr(w_down_scales), act, _ptr(y), _DT[y.dtype],
+              int(expected_rows), _stream(stream)))
     return y
 
 
 def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=None,
                     w_up_scales=None, w_down_scales=None, y=None, y_dtype=None, ws=None,
-                    expected_rows=0, stream=None):
-    """Both FFN stages with h held in the workspace ``ws``."""
+                    expected_rows=0, stream=None, cap_per_expert=None):
+    """Both FFN stages with h held in the workspace ``ws``.  cap_per_expert:
+    as in moe_ffn_gate_up (moe_grouped_ffn_masked)."""
     _dev(xd, "xd", ndim=2)
-    _dev(offsets, "offsets", torch.int32, 1)
     for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _dev(w, n, xd.dtype, 3)
     E_loc, H, I = _ffn_shapes(xd, w_gate, True)
     cap = xd.shape[0]
+    third = _rows_arg(offsets, cap_per_expert, E_loc, cap)
     act = _DT[xd.dtype]
     y_dtype = _y_dtype_for(act) if y_dtype is None else y_dtype
     if y is None:
@@ -267,12 +316,28 @@ def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=
     need = moe_ffn_workspace_bytes(cap, I, act)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=xd.device)
-    _check(lib().moe_grouped_ffn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, cap, H, I, act,
-                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
-                                 _ptr(w_up_scales), _ptr(w_down_scales), act, _ptr(y),
-                                 _DT[y.dtype], _ptr(ws), ws.numel() * ws.element_size(),
-                                 int(expected_rows), _stream(stream)))
+    fn = lib().moe_grouped_ffn if cap_per_expert is None else lib().moe_grouped_ffn_masked
+    _check(fn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, third, H, I, act,
+              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
+              _ptr(w_up_scales), _ptr(w_down_scales), act, _ptr(y),
+              _DT[y.dtype], _ptr(ws), ws.numel() * ws.element_size(),
+              int(expected_rows), _stream(stream)))
     return y
+
+
+def moe_ffn_gate_up_masked(xd, xd_scales, m, cap_per_expert, w_gate, w_up, **kw):
+    """moe_ffn_gate_up over the masked layout (rows [j*cap_per_expert, +m[j]))."""
+    return moe_ffn_gate_up(xd, xd_scales, m, w_gate, w_up, cap_per_expert=cap_per_expert, **kw)
+
+
+def moe_ffn_down_masked(h, h_scales, m, cap_per_expert, w_down, **kw):
+    """moe_ffn_down over the masked layout."""
+    return moe_ffn_down(h, h_scales, m, w_down, cap_per_expert=cap_per_expert, **kw)
+
+
+def moe_grouped_ffn_masked(xd, xd_scales, m, cap_per_expert, w_gate, w_up, w_down, **kw):
+    """moe_grouped_ffn over the masked layout."""
+    return moe_grouped_ffn(xd, xd_scales, m, w_gate, w_up, w_down, cap_per_expert=cap_per_expert, **kw)
 
 
 def moe_combine(y, row_of, topk_w, out=None, out_dtype=None, stream=None):

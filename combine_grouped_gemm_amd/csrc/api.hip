@@ -60,9 +60,18 @@ moe_status_t check_route_shape(int B, int E, int K) {
     return MOE_OK;
 }
 
-moe_status_t check_ffn_common(const void* a, const int32_t* offsets, int E_local, int cap_rows,
+// Where the rows of each local expert are: the contiguous layout's offsets
+// (E_local + 1), or the masked layout's valid-row counts m (E_local) with
+// fixed blocks of cap_e rows.
+struct Rows {
+    const int32_t* offsets;
+    const int32_t* m;
+    int cap_e;
+};
+
+moe_status_t check_ffn_common(const void* a, Rows rows, int E_local, int cap_rows,
                               int H, int I, moe_dtype_t act_dt, moe_dtype_t w_dt) {
-    REQUIRE(a && offsets, "null activation or offsets pointer");
+    REQUIRE(a && (rows.offsets || rows.m), "null activation or row-count pointer");
     REQUIRE(E_local >= 1 && E_local <= 1024, "E_local must be in [1, 1024] (got %d)", E_local);
     REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
     REQUIRE(H >= 64 && H % 64 == 0 && I >= 64 && I % 64 == 0,
@@ -82,14 +91,16 @@ moe_status_t check_y_dtype(moe_dtype_t act_dt, moe_dtype_t y_dt) {
     return MOE_OK;
 }
 
-moeep::FfnArgs ffn_args(const void* a, const float* a_scales, const int32_t* offsets, int E_local,
+moeep::FfnArgs ffn_args(const void* a, const float* a_scales, Rows rows, int E_local,
                         int cap_rows, int Kdim, int N, const void* w0, const void* w1,
                         const float* w0s, const float* w1s, void* out, float* out_scales,
                         int expected_rows) {
     moeep::FfnArgs f;
     f.a = a;
     f.a_scales = a_scales;
-    f.offsets = offsets;
+    f.offsets = rows.offsets;
+    f.m_counts = rows.m;
+    f.cap_e = rows.cap_e;
     f.E_loc = E_local;
     f.cap = cap_rows;
     f.Kdim = Kdim;
@@ -116,6 +127,71 @@ hipError_t run_ffn(const moeep::FfnArgs& f, moe_dtype_t act_dt, bool gated, hipS
 size_t elem_size(moe_dtype_t d) { return d == MOE_F32 ? 4 : d == MOE_BF16 ? 2 : 1; }
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+size_t ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt) {
+    if (cap_rows < 0 || I < 1) return 0;
+    size_t bytes = round256((size_t)cap_rows * I * elem_size(act_dt));
+    if (act_dt == MOE_FP8_E4M3) bytes += round256((size_t)cap_rows * ((I + 127) / 128) * sizeof(float));
+    return bytes;
+}
+
+moe_status_t ffn_gate_up(const void* xd, const float* xd_scales, Rows rows,
+                             int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
+                             const void* w_gate, const void* w_up, const float* w_gate_scales,
+                             const float* w_up_scales, moe_dtype_t w_dt, void* h, float* h_scales,
+                             int expected_rows, hipStream_t stream) {
+    moe_status_t s = check_ffn_common(xd, rows, E_local, cap_rows, H, I, act_dt, w_dt);
+    if (s != MOE_OK) return s;
+    REQUIRE(w_gate && w_up && h, "null weight or h pointer");
+    REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(h), "weights and h must be 16-byte aligned");
+    if (act_dt == MOE_FP8_E4M3)
+        REQUIRE(xd_scales && w_gate_scales && w_up_scales && h_scales, "fp8 needs all scale pointers");
+    auto f = ffn_args(xd, xd_scales, rows, E_local, cap_rows, H, I, w_gate, w_up, w_gate_scales,
+                      w_up_scales, h, h_scales, expected_rows);
+    return launched(run_ffn(f, act_dt, true, stream), "ffn gate/up");
+}
+
+moe_status_t ffn_down(const void* h, const float* h_scales, Rows rows, int E_local,
+                          int cap_rows, int H, int I, moe_dtype_t act_dt, const void* w_down,
+                          const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
+                          int expected_rows, hipStream_t stream) {
+    moe_status_t s = check_ffn_common(h, rows, E_local, cap_rows, H, I, act_dt, w_dt);
+    if (s != MOE_OK) return s;
+    s = check_y_dtype(act_dt, y_dt);
+    if (s != MOE_OK) return s;
+    REQUIRE(w_down && y, "null weight or y pointer");
+    REQUIRE(aligned16(w_down) && aligned16(y), "weights and y must be 16-byte aligned");
+    if (act_dt == MOE_FP8_E4M3) REQUIRE(h_scales && w_down_scales, "fp8 needs all scale pointers");
+    auto f = ffn_args(h, h_scales, rows, E_local, cap_rows, I, H, w_down, nullptr, w_down_scales,
+                      nullptr, y, nullptr, expected_rows);
+    return launched(run_ffn(f, act_dt, false, stream), "ffn down");
+}
+
+moe_status_t grouped_ffn(const void* xd, const float* xd_scales, Rows rows,
+                             int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const float* w_gate_scales, const float* w_up_scales,
+                             const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
+                             void* ws, size_t ws_bytes, int expected_rows, hipStream_t stream) {
+    moe_status_t s = check_ffn_common(xd, rows, E_local, cap_rows, H, I, act_dt, w_dt);
+    if (s != MOE_OK) return s;
+    s = check_y_dtype(act_dt, y_dt);
+    if (s != MOE_OK) return s;
+    REQUIRE(ws, "null workspace");
+    REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, "workspace must be 256-byte aligned");
+    const size_t need = ffn_workspace_bytes(cap_rows, I, act_dt);
+    REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    void* h = ws;
+    float* h_scales = nullptr;
+    if (act_dt == MOE_FP8_E4M3)
+        h_scales = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)cap_rows * I));
+    s = ffn_gate_up(xd, xd_scales, rows, E_local, cap_rows, H, I, act_dt, w_gate, w_up,
+                        w_gate_scales, w_up_scales, w_dt, h, h_scales, expected_rows, stream);
+    if (s != MOE_OK) return s;
+    return ffn_down(h, h_scales, rows, E_local, cap_rows, H, I, act_dt, w_down, w_down_scales,
+                        w_dt, y, y_dt, expected_rows, stream);
+}
+
 
 }  // namespace
 
@@ -167,6 +243,26 @@ moe_status_t moe_layout(const int32_t* topk_ids, int B, int K, int E, int e_begi
                     "moe_layout");
 }
 
+moe_status_t moe_layout_masked(const int32_t* topk_ids, int B, int K, int E, int e_begin, int e_end,
+                               int32_t* counts, int32_t* m, int32_t* row_of, int32_t* src_of,
+                               int cap_per_expert, void* ws, size_t ws_bytes, hipStream_t stream) {
+    moe_status_t s = check_route_shape(B, E, K);
+    if (s != MOE_OK) return s;
+    REQUIRE(e_begin >= 0 && e_begin < e_end && e_end <= E,
+            "need 0 <= e_begin < e_end <= E (got %d, %d, E=%d)", e_begin, e_end, E);
+    REQUIRE(cap_per_expert >= 1, "cap_per_expert must be >= 1 (got %d)", cap_per_expert);
+    REQUIRE((long long)(e_end - e_begin) * cap_per_expert <= 0x7fffffffLL,
+            "E_local * cap_per_expert must fit in int32");
+    REQUIRE(counts && m && src_of && ws, "null counts, m, src_of or workspace");
+    if (B > 0) REQUIRE(topk_ids && row_of, "null topk_ids or row_of");
+    REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, "workspace must be 256-byte aligned");
+    REQUIRE(ws_bytes >= moeep::layout_workspace_bytes(B, K, E),
+            "workspace too small: %zu < %zu bytes", ws_bytes, moeep::layout_workspace_bytes(B, K, E));
+    return launched(moeep::launch_layout_masked(topk_ids, B, K, E, e_begin, e_end, counts, m, row_of,
+                                                src_of, cap_per_expert, ws, stream),
+                    "moe_layout_masked");
+}
+
 moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int n_seg,
                           moe_dtype_t x_dt, int H, const int32_t* row_of, int K, void* xd,
                           moe_dtype_t xd_dt, float* xd_scales, int cap_rows, hipStream_t stream) {
@@ -205,10 +301,7 @@ moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int
 }
 
 size_t moe_ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt) {
-    if (cap_rows < 0 || I < 1) return 0;
-    size_t bytes = round256((size_t)cap_rows * I * elem_size(act_dt));
-    if (act_dt == MOE_FP8_E4M3) bytes += round256((size_t)cap_rows * ((I + 127) / 128) * sizeof(float));
-    return bytes;
+    return ffn_workspace_bytes(cap_rows, I, act_dt);
 }
 
 moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32_t* offsets,
@@ -216,31 +309,17 @@ moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32
                              const void* w_gate, const void* w_up, const float* w_gate_scales,
                              const float* w_up_scales, moe_dtype_t w_dt, void* h, float* h_scales,
                              int expected_rows, hipStream_t stream) {
-    moe_status_t s = check_ffn_common(xd, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
-    if (s != MOE_OK) return s;
-    REQUIRE(w_gate && w_up && h, "null weight or h pointer");
-    REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(h), "weights and h must be 16-byte aligned");
-    if (act_dt == MOE_FP8_E4M3)
-        REQUIRE(xd_scales && w_gate_scales && w_up_scales && h_scales, "fp8 needs all scale pointers");
-    auto f = ffn_args(xd, xd_scales, offsets, E_local, cap_rows, H, I, w_gate, w_up, w_gate_scales,
-                      w_up_scales, h, h_scales, expected_rows);
-    return launched(run_ffn(f, act_dt, true, stream), "moe_ffn_gate_up");
+    return ffn_gate_up(xd, xd_scales, Rows{offsets, nullptr, 0}, E_local, cap_rows, H, I, act_dt,
+                       w_gate, w_up, w_gate_scales, w_up_scales, w_dt, h, h_scales, expected_rows,
+                       stream);
 }
 
 moe_status_t moe_ffn_down(const void* h, const float* h_scales, const int32_t* offsets, int E_local,
                           int cap_rows, int H, int I, moe_dtype_t act_dt, const void* w_down,
                           const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
                           int expected_rows, hipStream_t stream) {
-    moe_status_t s = check_ffn_common(h, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
-    if (s != MOE_OK) return s;
-    s = check_y_dtype(act_dt, y_dt);
-    if (s != MOE_OK) return s;
-    REQUIRE(w_down && y, "null weight or y pointer");
-    REQUIRE(aligned16(w_down) && aligned16(y), "weights and y must be 16-byte aligned");
-    if (act_dt == MOE_FP8_E4M3) REQUIRE(h_scales && w_down_scales, "fp8 needs all scale pointers");
-    auto f = ffn_args(h, h_scales, offsets, E_local, cap_rows, I, H, w_down, nullptr, w_down_scales,
-                      nullptr, y, nullptr, expected_rows);
-    return launched(run_ffn(f, act_dt, false, stream), "moe_ffn_down");
+    return ffn_down(h, h_scales, Rows{offsets, nullptr, 0}, E_local, cap_rows, H, I, act_dt, w_down,
+                    w_down_scales, w_dt, y, y_dt, expected_rows, stream);
 }
 
 moe_status_t moe_grouped_ffn(const void* xd, const float* xd_scales, const int32_t* offsets,
@@ -249,23 +328,51 @@ moe_status_t moe_grouped_ffn(const void* xd, const float* xd_scales, const int32
                              const float* w_gate_scales, const float* w_up_scales,
                              const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
                              void* ws, size_t ws_bytes, int expected_rows, hipStream_t stream) {
-    moe_status_t s = check_ffn_common(xd, offsets, E_local, cap_rows, H, I, act_dt, w_dt);
-    if (s != MOE_OK) return s;
-    s = check_y_dtype(act_dt, y_dt);
-    if (s != MOE_OK) return s;
-    REQUIRE(ws, "null workspace");
-    REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, "workspace must be 256-byte aligned");
-    const size_t need = moe_ffn_workspace_bytes(cap_rows, I, act_dt);
-    REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-    void* h = ws;
-    float* h_scales = nullptr;
-    if (act_dt == MOE_FP8_E4M3)
-        h_scales = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)cap_rows * I));
-    s = moe_ffn_gate_up(xd, xd_scales, offsets, E_local, cap_rows, H, I, act_dt, w_gate, w_up,
-                        w_gate_scales, w_up_scales, w_dt, h, h_scales, expected_rows, stream);
-    if (s != MOE_OK) return s;
-    return moe_ffn_down(h, h_scales, offsets, E_local, cap_rows, H, I, act_dt, w_down, w_down_scales,
-                        w_dt, y, y_dt, expected_rows, stream);
+    return grouped_ffn(xd, xd_scales, Rows{offsets, nullptr, 0}, E_local, cap_rows, H, I, act_dt,
+                       w_gate, w_up, w_down, w_gate_scales, w_up_scales, w_down_scales, w_dt, y, y_dt,
+                       ws, ws_bytes, expected_rows, stream);
+}
+
+// masked layout: rows of local expert j are [j*cap_e, j*cap_e + m[j]) of E_local*cap_e
+#define MASKED_ROWS()                                                                          \
+    REQUIRE(cap_per_expert >= 1, "cap_per_expert must be >= 1 (got %d)", cap_per_expert);     \
+    REQUIRE(E_local >= 1 && E_local <= 1024, "E_local must be in [1, 1024] (got %d)", E_local); \
+    REQUIRE((long long)E_local * cap_per_expert <= 0x7fffffffLL, "E_local * cap_per_expert must fit in int32")
+
+moe_status_t moe_ffn_gate_up_masked(const void* xd, const float* xd_scales, const int32_t* m,
+                                    int E_local, int cap_per_expert, int H, int I, moe_dtype_t act_dt,
+                                    const void* w_gate, const void* w_up, const float* w_gate_scales,
+                                    const float* w_up_scales, moe_dtype_t w_dt, void* h,
+                                    float* h_scales, int expected_rows, hipStream_t stream) {
+    MASKED_ROWS();
+    REQUIRE(m, "null m");
+    return ffn_gate_up(xd, xd_scales, Rows{nullptr, m, cap_per_expert}, E_local, E_local * cap_per_expert,
+                       H, I, act_dt, w_gate, w_up, w_gate_scales, w_up_scales, w_dt, h, h_scales,
+                       expected_rows, stream);
+}
+
+moe_status_t moe_ffn_down_masked(const void* h, const float* h_scales, const int32_t* m, int E_local,
+                                 int cap_per_expert, int H, int I, moe_dtype_t act_dt,
+                                 const void* w_down, const float* w_down_scales, moe_dtype_t w_dt,
+                                 void* y, moe_dtype_t y_dt, int expected_rows, hipStream_t stream) {
+    MASKED_ROWS();
+    REQUIRE(m, "null m");
+    return ffn_down(h, h_scales, Rows{nullptr, m, cap_per_expert}, E_local, E_local * cap_per_expert,
+                    H, I, act_dt, w_down, w_down_scales, w_dt, y, y_dt, expected_rows, stream);
+}
+
+moe_status_t moe_grouped_ffn_masked(const void* xd, const float* xd_scales, const int32_t* m,
+                                    int E_local, int cap_per_expert, int H, int I, moe_dtype_t act_dt,
+                                    const void* w_gate, const void* w_up, const void* w_down,
+                                    const float* w_gate_scales, const float* w_up_scales,
+                                    const float* w_down_scales, moe_dtype_t w_dt, void* y,
+                                    moe_dtype_t y_dt, void* ws, size_t ws_bytes, int expected_rows,
+                                    hipStream_t stream) {
+    MASKED_ROWS();
+    REQUIRE(m, "null m");
+    return grouped_ffn(xd, xd_scales, Rows{nullptr, m, cap_per_expert}, E_local,
+                       E_local * cap_per_expert, H, I, act_dt, w_gate, w_up, w_down, w_gate_scales,
+                       w_up_scales, w_down_scales, w_dt, y, y_dt, ws, ws_bytes, expected_rows, stream);
 }
 
 moe_status_t moe_combine(const void* y, moe_dtype_t y_dt, int cap_rows, const int32_t* row_of,

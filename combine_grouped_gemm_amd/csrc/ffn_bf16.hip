@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
     const int wm = wave / WNW, wn = wave % WNW;
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
 
-    build_tile_prefix<NT, BM>(p.offsets, p.E_loc, cap, s_pre, s_tmp);
+    build_tile_prefix<NT, BM>(p, s_pre, s_tmp);
     const int n_tiles_n = (N + BNO - 1) / BNO;
     const int total = n_tiles_n * s_pre[p.E_loc];
 
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
     uint16_t* __restrict__ Out = static_cast<uint16_t*>(p.out);
 
     for (int tau = v; tau < total; tau += G) {
-        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p.E_loc, p.offsets, cap);
+        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
 

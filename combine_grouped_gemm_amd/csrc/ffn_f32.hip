@@ -20,7 +20,8 @@ __global__ __launch_bounds__(kCols * kRowGroups) void grouped_ffn_f32_kernel(Ffn
     const int col = blockIdx.y * kCols + threadIdx.x % kCols;
     const int g = threadIdx.x / kCols;
     if (col >= p.N) return;
-    const int r0 = clampi(p.offsets[j], 0, p.cap), r1 = clampi(p.offsets[j + 1], 0, p.cap);
+    int r0, r1;
+    expert_rows(p, j, r0, r1);
     const float* A = static_cast<const float*>(p.a);
     const float* w0 = static_cast<const float*>(p.w0) + ((size_t)j * p.N + col) * p.Kdim;
     const float* w1 = GATED ? static_cast<const float*>(p.w1) + ((size_t)j * p.N + col) * p.Kdim : nullptr;

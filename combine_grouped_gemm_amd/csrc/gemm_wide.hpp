@@ -116,7 +116,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
     const int nk = Kdim / BK;
 
-    build_tile_prefix<NT, BM>(p.offsets, p.E_loc, cap, s_pre, s_tmp);
+    build_tile_prefix<NT, BM>(p, s_pre, s_tmp);
     const int n_tiles_n = (N + BNO - 1) / BNO;
     const int total = n_tiles_n * s_pre[p.E_loc];
     const int G = gridDim.x;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     uint16_t* __restrict__ Out = static_cast<uint16_t*>(p.out);
 
     for (int tau = v; tau < total; tau += G) {
-        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p.E_loc, p.offsets, cap);
+        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
         const uint16_t* wg = W0 + (size_t)j * N * Kdim;

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     const bool k_tail = nk * ROWB != Kdim;          // last block holds 64 bytes
     const int nbN = (N + 127) / 128;
 
-    build_tile_prefix<NT, BM>(p.offsets, p.E_loc, cap, s_pre, s_tmp);
+    build_tile_prefix<NT, BM>(p, s_pre, s_tmp);
     const int n_tiles_n = (N + BNO - 1) / BNO;
     const int total = n_tiles_n * s_pre[p.E_loc];
     const int G = gridDim.x;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     const int lchunk = wide::swz(lane / 8, lane % 8);
 
     for (int tau = v; tau < total; tau += G) {
-        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p.E_loc, p.offsets, cap);
+        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
         const uint8_t* wg = W0 + (size_t)j * N * Kdim;

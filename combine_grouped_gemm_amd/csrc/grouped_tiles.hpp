@@ -1,6 +1,7 @@
 // Ragged tile scheduling shared by the grouped GEMM kernels.
 //
-// The per-expert row counts exist only on the device (offsets), so a
+// The per-expert row counts exist only on the device (offsets of the
+// contiguous layout, or the valid-row counts of the masked layout), so a
 // persistent grid derives its work list there: every block builds the
 // prefix sum over local experts of ceil(rows / BM) m-tiles in LDS and maps a
 // linear tile index tau to (expert j, n-tile, m-tile) by binary search, with
@@ -20,11 +21,24 @@ constexpr int kXcd = 8;
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Rows [r0, r1) of local expert j: a range of the contiguous layout, or the
+// first m_counts[j] rows of the expert's fixed block in the masked layout;
+// both clamped to the buffer.
+__device__ __forceinline__ void expert_rows(const FfnArgs& p, int j, int& r0, int& r1) {
+    if (p.offsets != nullptr) {
+        r0 = clampi(p.offsets[j], 0, p.cap);
+        r1 = clampi(p.offsets[j + 1], r0, p.cap);
+    } else {
+        r0 = j * p.cap_e;
+        r1 = r0 + clampi(p.m_counts[j], 0, p.cap_e);
+    }
+}
+
 // Block-wide exclusive prefix of m-tile counts per expert into s_pre[0..E_loc].
 // s_tmp needs NT / 64 ints.  Ends with a barrier.
 template <int NT, int BM>
-__device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E_loc, int cap,
-                                  int* s_pre, int* s_tmp) {
+__device__ void build_tile_prefix(const FfnArgs& p, int* s_pre, int* s_tmp) {
+    const int E_loc = p.E_loc;
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
     constexpr int NW = NT / kWave;
     int carry = 0;
@@ -33,9 +47,9 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E_loc
         const int j = base + tid;
         int v = 0;
         if (j < E_loc) {
-            const int r0 = clampi(offsets[j], 0, cap), r1 = clampi(offsets[j + 1], 0, cap);
-            const int n = r1 > r0 ? r1 - r0 : 0;
-            v = (n + BM - 1) / BM;
+            int r0, r1;
+            expert_rows(p, j, r0, r1);
+            v = (r1 - r0 + BM - 1) / BM;
         }
         int x = v;
 #pragma unroll
@@ -67,9 +81,8 @@ struct TileCoord {
 
 template <int BM>
 __device__ __forceinline__ TileCoord decode_tile(int tau, int n_tiles_n, const int* s_pre,
-                                                 int E_loc, const int32_t* __restrict__ offsets,
-                                                 int cap) {
-    int lo = 0, hi = E_loc;       // largest j with n_tiles_n * s_pre[j] <= tau
+                                                 const FfnArgs& p) {
+    int lo = 0, hi = p.E_loc;     // largest j with n_tiles_n * s_pre[j] <= tau
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (n_tiles_n * s_pre[mid] <= tau) lo = mid; else hi = mid;
@@ -80,7 +93,8 @@ __device__ __forceinline__ TileCoord decode_tile(int tau, int n_tiles_n, const i
     const int local = tau - n_tiles_n * s_pre[lo];
     t.nt = local / mt_j;
     const int mt = local % mt_j;
-    const int r0 = clampi(offsets[lo], 0, cap), r1 = clampi(offsets[lo + 1], 0, cap);
+    int r0, r1;
+    expert_rows(p, lo, r0, r1);
     // balanced split: m-tile mt of mt_j takes rows [n*mt/mt_j, n*(mt+1)/mt_j) of the
     // expert, at most ceil(n/mt_j) <= BM of them
     const int n = r1 - r0;

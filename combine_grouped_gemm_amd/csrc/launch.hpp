@@ -18,6 +18,11 @@ size_t layout_workspace_bytes(int B, int K, int E);
 hipError_t launch_layout(const int32_t* ids, int B, int K, int E, int e_begin, int e_end,
                          int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
                          int cap, void* ws, hipStream_t stream);
+// fixed-capacity variant: local expert j owns rows [j*cap_e, (j+1)*cap_e); m (E_loc) gets
+// min(count, cap_e)
+hipError_t launch_layout_masked(const int32_t* ids, int B, int K, int E, int e_begin, int e_end,
+                                int32_t* counts, int32_t* m, int32_t* row_of, int32_t* src_of,
+                                int cap_e, void* ws, hipStream_t stream);
 
 // dispatch.hip
 constexpr int kMaxSeg = 64;
@@ -39,7 +44,9 @@ hipError_t launch_combine(const void* y, int kind, const int32_t* row_of, const 
 struct FfnArgs {
     const void* a;            // activations (cap, Kdim)
     const float* a_scales;    // fp8 only: (cap, ceil(Kdim/128))
-    const int32_t* offsets;   // (E_loc + 1)
+    const int32_t* offsets;   // contiguous layout: (E_loc + 1); nullptr for the masked layout
+    const int32_t* m_counts;  // masked layout: (E_loc) valid rows of expert j, in [j*cap_e, ...)
+    int cap_e;                // masked layout: rows per expert block (cap = E_loc * cap_e)
     int E_loc, cap, Kdim, N;  // N = output columns (I for gate/up, H for down)
     const void* w0;           // gate or down (E_loc, N, Kdim)
     const void* w1;           // up (gate/up only)

@@ -22,6 +22,12 @@
 //             base of its expert plus the number of lower lanes holding the
 //             same expert, which keeps rows of an expert in ascending slot
 //             order.  Also fills src_of's padding rows with -1.
+//
+// The fixed-capacity ("masked") variant (SGLang "Expert Parallelism", the
+// MoE-runner table: masked layout for decode) runs the same three kernels;
+// local expert j owns rows [j*cap_e, (j+1)*cap_e), so the ranking needs no
+// offsets: a slot's row is j*cap_e + its rank within the expert, slots with
+// rank >= cap_e are dropped, and the scan also writes m[j] = min(count, cap_e).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -73,7 +79,9 @@ __global__ __launch_bounds__(kWave) void layout_hist_kernel(const int32_t* __res
 // One wave per expert: exclusive scan of the expert's chunk counts in place
 // (the chunk's first rank among the expert's slots); the total is counts[e].
 __global__ __launch_bounds__(kWave) void layout_scan_kernel(int nchunk, int32_t* __restrict__ base,
-                                                            int32_t* __restrict__ counts) {
+                                                            int32_t* __restrict__ counts, int e_begin,
+                                                            int e_end, int32_t* __restrict__ m,
+                                                            int cap_e) {
     const int lane = threadIdx.x, e = blockIdx.x;
     int32_t* row = base + (size_t)e * nchunk;
     int carry = 0;
@@ -89,11 +97,17 @@ __global__ __launch_bounds__(kWave) void layout_scan_kernel(int nchunk, int32_t*
         if (c < nchunk) row[c] = carry + x - v;
         carry += __shfl(x, kWave - 1, kWave);
     }
-    if (lane == 0) counts[e] = carry;
+    if (lane == 0) {
+        counts[e] = carry;
+        if (m != nullptr && e >= e_begin && e < e_end) m[e - e_begin] = carry < cap_e ? carry : cap_e;
+    }
 }
 
+// MASKED: cap is cap_e (rows per expert block) and offsets is unused.  Blocks
+// past the nchunk chunks only pad src_of.
+template <bool MASKED>
 __global__ __launch_bounds__(kWave) void layout_rank_kernel(
-    const int32_t* __restrict__ ids, int n_slots, int E, int e_begin, int e_end, int cap,
+    const int32_t* __restrict__ ids, int n_slots, int nchunk, int E, int e_begin, int e_end, int cap,
     const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_of, int32_t* __restrict__ src_of) {
     extern __shared__ int32_t s_next[];
@@ -101,9 +115,14 @@ __global__ __launch_bounds__(kWave) void layout_rank_kernel(
     const int E_loc = e_end - e_begin;
     const int s0 = blockIdx.x * kChunk;
     const int steps = s0 < n_slots ? kChunk : 0;     // an empty input still pads src_of
-    // local offsets: exclusive scan of counts[e_begin, e_end); plus this chunk's base
+    // MASKED: next rank per local expert = this chunk's base
+    // else:   local offsets (exclusive scan of counts[e_begin, e_end)) + the chunk's base
     int carry = 0;
-    for (int j0 = 0; j0 < E_loc; j0 += kWave) {
+    if (MASKED) {
+        for (int j = lane; j < E_loc; j += kWave)
+            s_next[j] = steps > 0 ? base[(size_t)(e_begin + j) * nchunk + blockIdx.x] : 0;
+    }
+    for (int j0 = 0; !MASKED && j0 < E_loc; j0 += kWave) {
         const int j = j0 + lane;
         const int v = j < E_loc ? counts[e_begin + j] : 0;
         int x = v;
@@ -115,12 +134,12 @@ __global__ __launch_bounds__(kWave) void layout_rank_kernel(
         if (j < E_loc) {
             const int off = carry + x - v;
             if (blockIdx.x == 0) offsets[j] = off;
-            s_next[j] = off + (steps > 0 ? base[(size_t)(e_begin + j) * gridDim.x + blockIdx.x] : 0);
+            s_next[j] = off + (steps > 0 ? base[(size_t)(e_begin + j) * nchunk + blockIdx.x] : 0);
         }
         carry += __shfl(x, kWave - 1, kWave);
     }
-    const int R = carry;                             // local rows
-    if (blockIdx.x == 0 && lane == 0) offsets[E_loc] = R;
+    const int R = carry;                             // local rows (contiguous layout)
+    if (!MASKED && blockIdx.x == 0 && lane == 0) offsets[E_loc] = R;
     __syncthreads();
     const int nbits = id_bits(E);
     for (int step = 0; step < steps; step += kWave) {
@@ -135,7 +154,10 @@ __global__ __launch_bounds__(kWave) void layout_rank_kernel(
             if (local) {
                 const int rank = popc64(m & lanemask_lt());
                 const int r = s_next[e - e_begin] + rank;
-                row = r < cap ? r : -1;
+                if (MASKED)
+                    row = r < cap ? (e - e_begin) * cap + r : -1;
+                else
+                    row = r < cap ? r : -1;
                 if (row >= 0) src_of[row] = s;
                 if (rank == 0) s_next[e - e_begin] = r + popc64(m);
             }
@@ -144,7 +166,15 @@ __global__ __launch_bounds__(kWave) void layout_rank_kernel(
         __syncthreads();
     }
     // padding rows of src_of
-    for (int r = R + blockIdx.x * kWave + lane; r < cap; r += gridDim.x * kWave) src_of[r] = -1;
+    if (MASKED) {
+        for (int r = blockIdx.x * kWave + lane; r < E_loc * cap; r += gridDim.x * kWave) {
+            const int j = r / cap, q = r - j * cap;
+            const int n = counts[e_begin + j];
+            if (q >= n) src_of[r] = -1;
+        }
+    } else {
+        for (int r = R + blockIdx.x * kWave + lane; r < cap; r += gridDim.x * kWave) src_of[r] = -1;
+    }
 }
 
 }  // namespace
@@ -165,10 +195,33 @@ hipError_t launch_layout(const int32_t* ids, int B, int K, int E, int e_begin, i
         hipLaunchKernelGGL(layout_hist_kernel, dim3(nchunk), dim3(kWave), E * sizeof(int32_t),
                            stream, ids, n_slots, E, w.base);
     }
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(E), dim3(kWave), 0, stream, nchunk, w.base, counts);
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(nchunk > 0 ? nchunk : 1), dim3(kWave),
-                       (e_end - e_begin) * sizeof(int32_t), stream, ids, n_slots, E, e_begin,
-                       e_end, cap, w.base, counts, offsets, row_of, src_of);
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(E), dim3(kWave), 0, stream, nchunk, w.base, counts,
+                       e_begin, e_end, (int32_t*)nullptr, 0);
+    hipLaunchKernelGGL(layout_rank_kernel<false>, dim3(nchunk > 0 ? nchunk : 1), dim3(kWave),
+                       (e_end - e_begin) * sizeof(int32_t), stream, ids, n_slots, nchunk, E,
+                       e_begin, e_end, cap, w.base, counts, offsets, row_of, src_of);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_masked(const int32_t* ids, int B, int K, int E, int e_begin, int e_end,
+                                int32_t* counts, int32_t* m, int32_t* row_of, int32_t* src_of,
+                                int cap_e, void* ws, hipStream_t stream) {
+    const int n_slots = B * K;
+    const int nchunk = n_chunks(n_slots);
+    LayoutWs w = carve(ws, nchunk, E);
+    if (nchunk > 0) {
+        hipLaunchKernelGGL(layout_hist_kernel, dim3(nchunk), dim3(kWave), E * sizeof(int32_t),
+                           stream, ids, n_slots, E, w.base);
+    }
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(E), dim3(kWave), 0, stream, nchunk, w.base, counts,
+                       e_begin, e_end, m, cap_e);
+    // enough blocks that the padding pass over E_local * cap_e rows is short
+    const long long rows = (long long)(e_end - e_begin) * cap_e;
+    const int pad_blocks = (int)((rows + 16 * kWave - 1) / (16 * kWave));
+    const int grid = nchunk > pad_blocks ? nchunk : (pad_blocks > 0 ? pad_blocks : 1);
+    hipLaunchKernelGGL(layout_rank_kernel<true>, dim3(grid), dim3(kWave),
+                       (e_end - e_begin) * sizeof(int32_t), stream, ids, n_slots, nchunk, E,
+                       e_begin, e_end, cap_e, w.base, counts, (int32_t*)nullptr, row_of, src_of);
     return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ from __future__ import annotations
 import torch
 
 from . import (FP8_BLOCK, moe_combine, moe_dispatch, moe_ffn_down, moe_ffn_gate_up,
-               moe_layout, moe_layout_workspace_bytes, moe_route)
+               moe_layout, moe_layout_masked, moe_layout_workspace_bytes, moe_route)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
@@ -25,17 +25,27 @@ class MoELayer:
     K per token; H hidden, I expert intermediate; local experts
     [e_begin, e_end); act_dtype stores Xd and h ('f32' | 'bf16' | 'fp8');
     y_dtype / out_dtype store the expert outputs and the combined rows.
+    layout: 'contiguous' (rows of the local experts back to back, cap_rows
+    rows, default T*K) or 'masked' (a fixed block of cap_per_expert rows per
+    local expert, default T -- no slot can be dropped).
     """
 
     def __init__(self, seg_rows, E, K, H, I, e_begin, e_end, act_dtype, y_dtype, out_dtype,
-                 device="cuda", cap_rows=None):
+                 device="cuda", cap_rows=None, layout="contiguous", cap_per_expert=None):
         self.seg_rows = tuple(int(b) for b in seg_rows)
         self.T = sum(self.seg_rows)
         self.E, self.K, self.H, self.I = E, K, H, I
         self.e_begin, self.e_end = e_begin, e_end
         self.E_loc = e_end - e_begin
         self.act_dtype, self.y_dtype, self.out_dtype = act_dtype, y_dtype, out_dtype
-        self.cap = self.T * K if cap_rows is None else int(cap_rows)
+        if layout not in ("contiguous", "masked"):
+            raise ValueError(f"unknown layout {layout!r}")
+        self.masked = layout == "masked"
+        self.cap_e = (max(self.T, 1) if cap_per_expert is None else int(cap_per_expert)) if self.masked else None
+        if self.masked:
+            self.cap = self.E_loc * self.cap_e
+        else:
+            self.cap = self.T * K if cap_rows is None else int(cap_rows)
         # rows a local expert gets under balanced routing: the FFN tile-shape hint
         self.expected_rows = max(1, (self.T * K) // E)
         dev = torch.device(device)
@@ -44,7 +54,7 @@ class MoELayer:
         self.topk_ids = torch.empty((T, K), **i32)
         self.topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
         self.counts = torch.empty(E, **i32)
-        self.offsets = torch.empty(self.E_loc + 1, **i32)
+        self.offsets = torch.empty(self.E_loc + 1, **i32)     # contiguous: offsets; masked: m (E_loc)
         self.row_of = torch.empty((T, K), **i32)
         self.src_of = torch.empty(cap, **i32)
         self.layout_ws = torch.empty(max(moe_layout_workspace_bytes(T, K, E), 256),
@@ -63,21 +73,31 @@ class MoELayer:
         moe_route(logits, self.K, self.topk_ids, self.topk_w, stream=stream)
 
     def layout(self, stream=None):
-        moe_layout(self.topk_ids, self.E, self.e_begin, self.e_end, self.cap, self.counts,
-                   self.offsets, self.row_of, self.src_of, self.layout_ws, stream=stream)
+        if self.masked:
+            moe_layout_masked(self.topk_ids, self.E, self.e_begin, self.e_end, self.cap_e, self.counts,
+                              self.offsets[:self.E_loc], self.row_of, self.src_of, self.layout_ws,
+                              stream=stream)
+        else:
+            moe_layout(self.topk_ids, self.E, self.e_begin, self.e_end, self.cap, self.counts,
+                       self.offsets, self.row_of, self.src_of, self.layout_ws, stream=stream)
+
+    @property
+    def rows(self):
+        """The FFN's row description: offsets (contiguous) or m (masked)."""
+        return self.offsets[:self.E_loc] if self.masked else self.offsets
 
     def dispatch(self, x_segments, stream=None):
         moe_dispatch(x_segments, self.row_of, self.cap, self.act_dtype, self.xd, self.xd_scales,
                      stream=stream)
 
     def gate_up(self, w, stream=None):
-        moe_ffn_gate_up(self.xd, self.xd_scales, self.offsets, w["gate"], w["up"],
+        moe_ffn_gate_up(self.xd, self.xd_scales, self.rows, w["gate"], w["up"],
                         w.get("gate_scale"), w.get("up_scale"), self.h, self.h_scales,
-                        expected_rows=self.expected_rows, stream=stream)
+                        expected_rows=self.expected_rows, stream=stream, cap_per_expert=self.cap_e)
 
     def down(self, w, stream=None):
-        moe_ffn_down(self.h, self.h_scales, self.offsets, w["down"], w.get("down_scale"), self.y,
-                     expected_rows=self.expected_rows, stream=stream)
+        moe_ffn_down(self.h, self.h_scales, self.rows, w["down"], w.get("down_scale"), self.y,
+                     expected_rows=self.expected_rows, stream=stream, cap_per_expert=self.cap_e)
 
     def combine(self, stream=None):
         moe_combine(self.y, self.row_of, self.topk_w, self.out, stream=stream)

@@ -113,6 +113,32 @@ moe_status_t moe_layout(const int32_t* topk_ids, int B, int K, int E, int e_begi
                         int cap_rows, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_layout_masked -- the fixed-capacity ("masked") layout.  [SGLang]
+ * MoE-runner table: the grouped GEMM takes a contiguous layout for prefill
+ * and a masked layout for decode; the dispatch paragraph pairs the
+ * low-latency decode mode with graph capture.  Local expert j owns the fixed
+ * row block [j*cap_per_expert, (j+1)*cap_per_expert) of an
+ * (E_local*cap_per_expert)-row buffer, so no prefix sum is needed and every
+ * size is static.
+ *   counts   (E) int32 out: slots routed to each expert (all E experts).
+ *   m        (E_local) int32 out: valid rows of local expert j,
+ *            min(counts[e_begin + j], cap_per_expert) -- the mask.
+ *   row_of   (B, K) int32 out: j*cap_per_expert + rank of (t, k) among its
+ *            expert's slots in (t, k) order; -1 for non-local slots and for
+ *            slots with rank >= cap_per_expert (dropped, still counted).
+ *   src_of   (E_local*cap_per_expert) int32 out: slot t*K+k of each row, -1
+ *            for rows past m[j] in each block.
+ *   ws       as for moe_layout (moe_layout_workspace_bytes(B, K, E)).
+ * Arguments are checked as for moe_layout, plus cap_per_expert >= 1 and
+ * E_local*cap_per_expert < 2^31.  moe_dispatch and moe_combine take this
+ * row_of unchanged with cap_rows = E_local*cap_per_expert; the FFN takes m
+ * through the *_masked entry points below.
+ */
+moe_status_t moe_layout_masked(const int32_t* topk_ids, int B, int K, int E, int e_begin, int e_end,
+                               int32_t* counts, int32_t* m, int32_t* row_of, int32_t* src_of,
+                               int cap_per_expert, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * moe_dispatch -- scatter token rows into the dense expert-contiguous
  * buffer that feeds the grouped GEMM.  [Anatomy] "Dispatch": the tokens for
  * the local experts are gathered into one dense buffer so the grouped GEMM
@@ -184,6 +210,33 @@ moe_status_t moe_grouped_ffn(const void* xd, const float* xd_scales, const int32
                              const float* w_down_scales, moe_dtype_t w_dt,
                              void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
                              int expected_rows, hipStream_t stream);
+
+/*
+ * The same three calls over the masked layout of moe_layout_masked: local
+ * expert j's rows are [j*cap_per_expert, j*cap_per_expert + m[j]) of
+ * buffers with E_local*cap_per_expert rows (xd, h, y and their scales);
+ * m (E_local, device) is read on the device and clamped to
+ * [0, cap_per_expert].  Everything else -- weights, dtypes, numerics,
+ * workspace (moe_ffn_workspace_bytes(E_local*cap_per_expert, I, act_dt)),
+ * expected_rows -- is as above.  Rows past m[j] in a block are not written.
+ */
+moe_status_t moe_ffn_gate_up_masked(const void* xd, const float* xd_scales, const int32_t* m,
+                                    int E_local, int cap_per_expert, int H, int I, moe_dtype_t act_dt,
+                                    const void* w_gate, const void* w_up,
+                                    const float* w_gate_scales, const float* w_up_scales,
+                                    moe_dtype_t w_dt, void* h, float* h_scales, int expected_rows,
+                                    hipStream_t stream);
+moe_status_t moe_ffn_down_masked(const void* h, const float* h_scales, const int32_t* m,
+                                 int E_local, int cap_per_expert, int H, int I, moe_dtype_t act_dt,
+                                 const void* w_down, const float* w_down_scales, moe_dtype_t w_dt,
+                                 void* y, moe_dtype_t y_dt, int expected_rows, hipStream_t stream);
+moe_status_t moe_grouped_ffn_masked(const void* xd, const float* xd_scales, const int32_t* m,
+                                    int E_local, int cap_per_expert, int H, int I, moe_dtype_t act_dt,
+                                    const void* w_gate, const void* w_up, const void* w_down,
+                                    const float* w_gate_scales, const float* w_up_scales,
+                                    const float* w_down_scales, moe_dtype_t w_dt,
+                                    void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
+                                    int expected_rows, hipStream_t stream);
 
 /*
  * moe_combine -- gate-weighted gather-reduce back to token order.

@@ -103,3 +103,23 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         m.moe_route(torch.zeros(4, 8), 2)
+
+
+def test_masked_entry_points_reject():
+    L = m.lib()
+    p = ctypes.c_void_p(4096)
+    # layout: cap_per_expert must be >= 1, E_local * cap_per_expert must fit in int32
+    assert L.moe_layout_masked(p, 4, 2, 8, 0, 8, p, p, p, p, 0, p, 1 << 20, None) == m.MOE_ERR_INVALID_ARG
+    assert "cap_per_expert" in L.moe_last_error().decode()
+    assert L.moe_layout_masked(p, 4, 2, 1024, 0, 1024, p, p, p, p, 1 << 22, p, 1 << 20, None) == 1
+    assert "fit in int32" in L.moe_last_error().decode()
+    assert L.moe_layout_masked(p, 4, 2, 8, 0, 8, p, None, p, p, 4, p, 1 << 20, None) == 1
+    assert "null" in L.moe_last_error().decode()
+    # FFN: m must be given; the shared checks still apply
+    assert L.moe_ffn_gate_up_masked(p, None, None, 4, 16, 128, 128, 1, p, p, None, None, 1, p,
+                                    None, 0, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_ffn_down_masked(p, None, p, 4, 0, 128, 128, 1, p, None, 1, p, 1, 0, None) == 1
+    assert "cap_per_expert" in L.moe_last_error().decode()
+    assert L.moe_grouped_ffn_masked(p, None, p, 4, 16, 100, 128, 1, p, p, p, None, None, None, 1,
+                                    p, 1, p, 1 << 30, 0, None) == m.MOE_ERR_INVALID_ARG
+    assert "multiples of 64" in L.moe_last_error().decode()
