@@ -23,14 +23,18 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                  construction) shifted to fixed row blocks; overflow keeps the
                  first cap_e slots of an expert in (t, k) order.
   dispatch/combine pinned: identity-expert round trip returns x * sum(gates).
+  eplb           expert placement (Moreh report, load balancing between GPUs):
+                 pinned by a hand-worked case, a perfect split, exhaustive
+                 optima of small instances, and the report's outcome (2x ->
+                 within 5%) on the EP-share workload's routing.
   expert_ffn     pinned: dense SwiGLU via torch CPU, pure-Python brute force.
   numerics       pinned: exhaustive bf16 / e4m3 casts against torch.
   fp8 block geometry and scale rule: parity unpinned by the pages (a reading
   both sides implement); its properties are checked.
 """
-from . import numerics
+from . import eplb, numerics
 from .moe import (route, layout, layout_masked, dispatch, silu, expert_ffn, grouped_ffn,
                   grouped_ffn_masked, combine, layer)
 
-__all__ = ["numerics", "route", "layout", "layout_masked", "dispatch", "silu", "expert_ffn",
+__all__ = ["eplb", "numerics", "route", "layout", "layout_masked", "dispatch", "silu", "expert_ffn",
            "grouped_ffn", "grouped_ffn_masked", "combine", "layer"]

@@ -165,6 +165,24 @@ def gen_logits(cfg: MoEConfig, x_segments=None, bias_params=None) -> torch.Tenso
     return logits.contiguous()
 
 
+def gen_calibration_logits(cfg: MoEConfig, seed_offset: int = 1000, batches: int = 1) -> torch.Tensor:
+    """Router logits of other batches of the same model: ``batches`` batches
+    of the workload's size, tokens drawn with seeds seed + seed_offset + b,
+    the workload's own router weights and logit bias.  Expert activation
+    counts measured on them drive expert placement."""
+    w_r = gen_router(cfg)
+    bias_params = zipf_bias_params(cfg)
+    bias = zipf_bias(cfg, *bias_params)[None, :] if bias_params else None
+    out = []
+    for b in range(batches):
+        other = replace(cfg, seed=cfg.seed + seed_offset + b)
+        x = torch.cat([s.float() for s in gen_x(other)], dim=0)
+        lg = x @ w_r.T
+        out.append(lg + bias if bias is not None else lg)
+        del x
+    return torch.cat(out, dim=0).contiguous()
+
+
 # ----------------------------------------------------------------------------
 # expert weights
 # ----------------------------------------------------------------------------
@@ -200,8 +218,12 @@ def _expert_generator(cfg: MoEConfig, e_global: int, which: int, device) -> torc
     return g
 
 
-def gen_expert_weights(cfg: MoEConfig, device="cpu") -> ExpertWeights:
+def gen_expert_weights(cfg: MoEConfig, device="cpu", experts=None) -> ExpertWeights:
     """Expert weights drawn on ``device``, N(0, 1/fan_in) in value.
+
+    ``experts`` lists the (logical) expert of each local slot; default the
+    local range [e_begin, e_end).  A placement that renumbers experts passes
+    the logical expert held by each local physical slot.
 
     Each (expert, matrix) pair has its own seeded generator, so a workload's
     weights are the same whichever subset of experts is drawn, but they
@@ -212,12 +234,13 @@ def gen_expert_weights(cfg: MoEConfig, device="cpu") -> ExpertWeights:
     s = (1 / (64 * sqrt(fan_in))) * exp(0.1 * N(0, 1)), so code * scale has
     roughly the N(0, 1/fan_in) spread of the other workloads.
     """
-    E_loc, H, I = cfg.E_loc, cfg.H, cfg.I
+    experts = list(range(cfg.e_begin, cfg.e_end)) if experts is None else [int(e) for e in experts]
+    E_loc, H, I = len(experts), cfg.H, cfg.I
     shapes = ((I, H), (I, H), (H, I))
     if cfg.w_dtype in ("f32", "bf16"):
         dt = _storage(cfg.w_dtype)
         mats = [torch.empty((E_loc,) + s, dtype=dt, device=device) for s in shapes]
-        for j, e in enumerate(range(cfg.e_begin, cfg.e_end)):
+        for j, e in enumerate(experts):
             for w, (m, s) in enumerate(zip(mats, shapes)):
                 g = _expert_generator(cfg, e, w, device)
                 m[j].copy_((torch.randn(s, generator=g, device=device) / math.sqrt(s[1])).to(dt))
@@ -228,7 +251,7 @@ def gen_expert_weights(cfg: MoEConfig, device="cpu") -> ExpertWeights:
             nb = -(-s[1] // FP8_BLOCK)
             codes.append(torch.empty((E_loc,) + s, dtype=torch.float8_e4m3fn, device=device))
             scales.append(torch.empty((E_loc, s[0], nb), dtype=torch.float32, device=device))
-        for j, e in enumerate(range(cfg.e_begin, cfg.e_end)):
+        for j, e in enumerate(experts):
             for w, s in enumerate(shapes):
                 g = _expert_generator(cfg, e, w, device)
                 c = (torch.randn(s, generator=g, device=device) * 64.0).clamp_(-448.0, 448.0)
