@@ -51,6 +51,8 @@ def parse():
                     help="masked layout: rows per expert block (default T, nothing dropped)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step as a HIP graph and time its replays")
+    ap.add_argument("--eplb", action="store_true",
+                    help="balanced expert placement from 8 calibration batches (EP-share workloads)")
     return ap.parse_args()
 
 
@@ -125,6 +127,45 @@ def measured_copy_gbs(dev, mib=1024, reps=5):
     gbs = 2 * src.numel() * 4 * reps / (t0.elapsed_time(t1) / 1e3) / 1e9
     del src, dst
     return gbs
+
+
+def _group_loads(counts, G):
+    c = np.asarray(counts, dtype=np.int64)
+    return c.reshape(G, -1).sum(axis=1)
+
+
+def eplb_placement(m, cfg, dev, batches=8):
+    """Balanced placement of the experts over E / E_loc ranks from the
+    activation counts of `batches` calibration batches, all counted by the
+    library (route + layout on the GPU) and placed by moe_eplb_place."""
+    G = cfg.E // cfg.E_loc
+    if G * cfg.E_loc != cfg.E or cfg.e_begin % cfg.E_loc:
+        raise SystemExit("--eplb needs a local range that is one of E / E_loc equal groups")
+    lg = wl.gen_calibration_logits(cfg, 1000, batches=batches).to(dev)
+    ids, _ = m.moe_route(lg, cfg.K)
+    lay = m.moe_layout(ids, cfg.E, 0, cfg.E, ids.numel())
+    counts = lay["counts"].cpu().numpy()
+    phys = m.moe_eplb_place(counts, G).numpy()
+    logical_of_phys = np.argsort(phys)
+    return {"G": G, "phys": phys, "map": torch.from_numpy(phys.astype(np.int32)).to(dev),
+            "local_logical": [int(e) for e in logical_of_phys[cfg.e_begin:cfg.e_end]],
+            "calib_counts": counts}
+
+
+def eplb_report(m, cfg, logits, placement, layer):
+    """Per-rank loads of the measured batch with contiguous expert chunks and
+    with the placement (counts from the library's layout of each routing)."""
+    G = placement["G"]
+    ids, _ = m.moe_route(logits, cfg.K)
+    before = _group_loads(m.moe_layout(ids, cfg.E, 0, cfg.E, ids.numel())["counts"].cpu().numpy(), G)
+    after = _group_loads(layer.counts.cpu().numpy(), G)
+
+    def stats(gl):
+        gl = gl.astype(np.float64)
+        return {"loads": [int(v) for v in gl], "max_over_min": round(float(gl.max() / gl.min()), 4),
+                "balancedness": round(float(gl.mean() / gl.max()), 4)}
+    return {"ranks": G, "contiguous_chunks": stats(before), "balanced_placement": stats(after),
+            "calibration": "8 batches of the workload's size, other tokens, same router and bias"}
 
 
 def graph_replay(layer, x, logits, wdict, steps, warmup):
@@ -242,13 +283,20 @@ def main():
     logits_cpu = wl.gen_logits(cfg, x_cpu)
     x = [s.to(dev) for s in x_cpu]
     logits = logits_cpu.to(dev)
-    W = wl.gen_expert_weights(cfg, device=dev)
+    placement = None
+    if a.eplb:
+        placement = eplb_placement(m, cfg, dev)
+        W = wl.gen_expert_weights(cfg, device=dev, experts=placement["local_logical"])
+    else:
+        W = wl.gen_expert_weights(cfg, device=dev)
     wdict = {"gate": W.gate, "up": W.up, "down": W.down}
     if cfg.w_dtype == "fp8":
         wdict.update(gate_scale=W.gate_scale, up_scale=W.up_scale, down_scale=W.down_scale)
     layer = m.MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end,
                        cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=dev, layout=a.layout,
                        cap_per_expert=(a.cap_per_expert or None))
+    if placement is not None:
+        layer.expert_map = placement["map"]
     stages = layer.stages(x, logits, wdict)
 
     # parity gate before timing: routing and layout must equal the oracle's
@@ -256,6 +304,8 @@ def main():
     torch.cuda.synchronize()
     import oracle
     ids, _ = oracle.route(logits_cpu.numpy(), cfg.K)
+    if placement is not None:
+        ids = placement["phys"][ids]
     lay = oracle.layout(ids, cfg.E, cfg.e_begin, cfg.e_end, cfg.cap)
     ref_row_of = (oracle.layout_masked(ids, cfg.E, cfg.e_begin, cfg.e_end, layer.cap_e)["row_of"]
                   if layer.masked else lay["row_of"])
@@ -338,6 +388,9 @@ def main():
     }
     if a.layout == "masked":
         res["config"]["layout"] = {"kind": "masked", "cap_per_expert": layer.cap_e}
+    if placement is not None:
+        res["config"]["placement"] = "balanced (8 calibration batches)"
+        res["eplb"] = eplb_report(m, cfg, logits, placement, layer)
     if a.graph:
         res["graph_replay"] = graph_replay(layer, x, logits, wdict, a.steps, a.warmup)
     if a.copy_calibration_mib:

@@ -20,7 +20,8 @@ __all__ = ["MoeError", "lib", "library_path", "moe_version", "moe_route",
            "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
            "moe_ffn_workspace_bytes", "moe_ffn_gate_up", "moe_ffn_down",
            "moe_grouped_ffn", "moe_combine", "moe_layout_masked", "moe_ffn_gate_up_masked",
-           "moe_ffn_down_masked", "moe_grouped_ffn_masked", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
+           "moe_ffn_down_masked", "moe_grouped_ffn_masked", "moe_route_mapped", "moe_eplb_place",
+           "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
            "MoELayer"]
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
         "moe_grouped_ffn": ([P, P, P, I, I, I, I, I, P, P, P, P, P, P, I, P, I, P, Z, I, P], S),
         "moe_combine": ([P, I, I, P, P, I, I, I, P, I, P], S),
         "moe_layout_masked": ([P, I, I, I, I, I, P, P, P, P, I, P, Z, P], S),
+        "moe_route_mapped": ([P, I, I, I, P, P, P, P], S),
+        "moe_eplb_place": ([P, I, I, P], S),
     }
     # the masked FFN calls take (m, E_local, cap_per_expert) where the others take
     # (offsets, E_local, cap_rows): same argument types
@@ -139,6 +142,36 @@ def moe_route(logits, K: int, topk_ids=None, topk_w=None, stream=None):
     _dev(topk_w, "topk_w", torch.float32)
     _check(lib().moe_route(_ptr(logits), B, E, K, _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
     return topk_ids, topk_w
+
+
+def moe_route_mapped(logits, K: int, phys_of_logical, topk_ids=None, topk_w=None, stream=None):
+    """moe_route with the chosen expert ids written through a placement map
+    (phys_of_logical: (E,) int32 device tensor)."""
+    _dev(logits, "logits", torch.float32, 2)
+    _dev(phys_of_logical, "phys_of_logical", torch.int32, 1)
+    B, E = logits.shape
+    if phys_of_logical.numel() != E:
+        raise ValueError("phys_of_logical needs E entries")
+    if topk_ids is None:
+        topk_ids = torch.empty((B, K), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((B, K), dtype=torch.float32, device=logits.device)
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    _dev(topk_w, "topk_w", torch.float32, 2)
+    _check(lib().moe_route_mapped(_ptr(logits), B, E, K, _ptr(phys_of_logical), _ptr(topk_ids),
+                                  _ptr(topk_w), _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_eplb_place(load, n_groups: int):
+    """Host expert placement: load (E,) activation counts (any integer
+    array-like) -> phys_of_logical (E,) int32 CPU tensor."""
+    load = torch.as_tensor(load).to(torch.int64).contiguous().cpu()
+    if load.dim() != 1:
+        raise ValueError("load must be 1-D")
+    phys = torch.empty(load.numel(), dtype=torch.int32)
+    _check(lib().moe_eplb_place(load.data_ptr(), load.numel(), int(n_groups), phys.data_ptr()))
+    return phys
 
 
 def moe_layout_workspace_bytes(B: int, K: int, E: int) -> int:

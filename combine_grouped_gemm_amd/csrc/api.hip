@@ -216,7 +216,28 @@ moe_status_t moe_route(const float* logits, int B, int E, int K, int32_t* topk_i
     moe_status_t s = check_route_shape(B, E, K);
     if (s != MOE_OK) return s;
     if (B > 0) REQUIRE(logits && topk_ids && topk_w, "null pointer argument");
-    return launched(moeep::launch_route(logits, B, E, K, topk_ids, topk_w, stream), "moe_route");
+    return launched(moeep::launch_route(logits, B, E, K, topk_ids, topk_w, nullptr, stream), "moe_route");
+}
+
+moe_status_t moe_route_mapped(const float* logits, int B, int E, int K, const int32_t* phys_of_logical,
+                              int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+    moe_status_t s = check_route_shape(B, E, K);
+    if (s != MOE_OK) return s;
+    REQUIRE(phys_of_logical, "null phys_of_logical");
+    if (B > 0) REQUIRE(logits && topk_ids && topk_w, "null pointer argument");
+    return launched(moeep::launch_route(logits, B, E, K, topk_ids, topk_w, phys_of_logical, stream),
+                    "moe_route_mapped");
+}
+
+moe_status_t moe_eplb_place(const int64_t* load, int E, int n_groups, int32_t* phys_of_logical) {
+    REQUIRE(E >= 1 && E <= 1024, "E must be in [1, 1024] (got %d)", E);
+    REQUIRE(n_groups >= 1 && E % n_groups == 0, "n_groups must divide E (got E=%d, n_groups=%d)", E,
+            n_groups);
+    REQUIRE(load && phys_of_logical, "null load or phys_of_logical");
+    for (int e = 0; e < E; ++e) REQUIRE(load[e] >= 0, "load[%d] < 0", e);
+    moeep::place_experts(load, E, n_groups, phys_of_logical);
+    g_last_error[0] = '\0';
+    return MOE_OK;
 }
 
 size_t moe_layout_workspace_bytes(int B, int K, int E) {

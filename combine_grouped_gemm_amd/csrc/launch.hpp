@@ -9,9 +9,12 @@
 
 namespace moeep {
 
-// route.hip
+// route.hip (map: optional (E) device table logical -> physical expert id)
 hipError_t launch_route(const float* logits, int B, int E, int K, int32_t* ids, float* w,
-                        hipStream_t stream);
+                        const int32_t* map, hipStream_t stream);
+
+// placement.hip (host): balanced equal-size expert groups, see the file header
+bool place_experts(const int64_t* load, int E, int G, int32_t* phys_of_logical);
 
 // layout.hip
 size_t layout_workspace_bytes(int B, int K, int E);

@@ -9,7 +9,10 @@
 // in the low word), so one unsigned max selects the largest logit with the
 // lowest id.  K rounds of "local max -> wave max by xor shuffles -> owner
 // clears its key" produce the picks in order; gates come from the selected
-// values with fp32 expf, written coalesced at the end.
+// values with fp32 expf, written coalesced at the end.  With a placement map
+// (Moreh report, load balancing between GPUs: the router emits the renumbered
+// expert ids) the chosen ids are written through it; selection and gates are
+// unchanged.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -38,7 +41,7 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 template <int EPL>
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const float* __restrict__ logits, int B, int E, int K, int32_t* __restrict__ ids,
-    float* __restrict__ w) {
+    float* __restrict__ w, const int32_t* __restrict__ map) {
     // dynamic LDS: per wave K gate numerators, then per wave K ids
     extern __shared__ char smem[];
     const int wave = threadIdx.x / kWave;
@@ -85,31 +88,31 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     const float inv = 1.0f / sum;
     for (int k = lane; k < K; k += kWave) {
-        ids[(size_t)t * K + k] = s_id[k];
+        ids[(size_t)t * K + k] = map != nullptr ? map[s_id[k]] : s_id[k];
         w[(size_t)t * K + k] = s_val[k] * inv;
     }
 }
 
 template <int EPL>
 hipError_t launch_epl(const float* logits, int B, int E, int K, int32_t* ids, float* w,
-                      hipStream_t stream) {
+                      const int32_t* map, hipStream_t stream) {
     dim3 grid((B + kRouteWaves - 1) / kRouteWaves), block(kRouteWaves * kWave);
     const size_t lds = (size_t)kRouteWaves * K * (sizeof(float) + sizeof(int));
-    hipLaunchKernelGGL(route_kernel<EPL>, grid, block, lds, stream, logits, B, E, K, ids, w);
+    hipLaunchKernelGGL(route_kernel<EPL>, grid, block, lds, stream, logits, B, E, K, ids, w, map);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, int B, int E, int K, int32_t* ids, float* w,
-                        hipStream_t stream) {
+                        const int32_t* map, hipStream_t stream) {
     if (B == 0) return hipSuccess;
     const int epl = (E + kWave - 1) / kWave;
-    if (epl <= 1) return launch_epl<1>(logits, B, E, K, ids, w, stream);
-    if (epl <= 2) return launch_epl<2>(logits, B, E, K, ids, w, stream);
-    if (epl <= 4) return launch_epl<4>(logits, B, E, K, ids, w, stream);
-    if (epl <= 8) return launch_epl<8>(logits, B, E, K, ids, w, stream);
-    return launch_epl<16>(logits, B, E, K, ids, w, stream);
+    if (epl <= 1) return launch_epl<1>(logits, B, E, K, ids, w, map, stream);
+    if (epl <= 2) return launch_epl<2>(logits, B, E, K, ids, w, map, stream);
+    if (epl <= 4) return launch_epl<4>(logits, B, E, K, ids, w, map, stream);
+    if (epl <= 8) return launch_epl<8>(logits, B, E, K, ids, w, map, stream);
+    return launch_epl<16>(logits, B, E, K, ids, w, map, stream);
 }
 
 }  // namespace moeep

@@ -13,7 +13,8 @@ from __future__ import annotations
 import torch
 
 from . import (FP8_BLOCK, moe_combine, moe_dispatch, moe_ffn_down, moe_ffn_gate_up,
-               moe_layout, moe_layout_masked, moe_layout_workspace_bytes, moe_route)
+               moe_layout, moe_layout_masked, moe_layout_workspace_bytes, moe_route,
+               moe_route_mapped)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
@@ -67,10 +68,16 @@ class MoELayer:
         self.h_scales = torch.empty((cap, -(-I // FP8_BLOCK)), dtype=torch.float32, device=dev) if fp8 else None
         self.y = torch.empty((cap, H), dtype=_TORCH[y_dtype], device=dev)
         self.out = torch.empty((T, H), dtype=_TORCH[out_dtype], device=dev)
+        # placement map (E,) int32 on the device, logical -> physical expert id; when
+        # set, routing emits physical ids and [e_begin, e_end) is a physical range
+        self.expert_map = None
 
     # individual stages (each one library call) ---------------------------------
     def route(self, logits, stream=None):
-        moe_route(logits, self.K, self.topk_ids, self.topk_w, stream=stream)
+        if self.expert_map is None:
+            moe_route(logits, self.K, self.topk_ids, self.topk_w, stream=stream)
+        else:
+            moe_route_mapped(logits, self.K, self.expert_map, self.topk_ids, self.topk_w, stream=stream)
 
     def layout(self, stream=None):
         if self.masked:

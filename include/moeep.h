@@ -107,6 +107,37 @@ moe_status_t moe_route(const float* logits, int B, int E, int K,
  *   ws / ws_bytes: device workspace of at least
  *   moe_layout_workspace_bytes(B, K, E) bytes, 256-byte aligned.
  */
+/*
+ * moe_route_mapped -- moe_route with a placement map.  [Moreh] load
+ * balancing between GPUs: experts are renumbered so each rank's set is a
+ * contiguous id range, and the gating network emits the renumbered ids.
+ * Selection, slot order, ties and gates are exactly those of moe_route on
+ * the logical ids; each chosen id e is written as phys_of_logical[e].
+ *   phys_of_logical (E) int32 device table, a permutation of [0, E) (e.g.
+ *   from moe_eplb_place); entries are used as given.
+ * Errors as for moe_route, plus a null phys_of_logical.
+ */
+moe_status_t moe_route_mapped(const float* logits, int B, int E, int K, const int32_t* phys_of_logical,
+                              int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/*
+ * moe_eplb_place -- expert placement for load balancing (host function; no
+ * GPU work).  [Moreh] load balancing between GPUs: group E experts into
+ * n_groups sets of E/n_groups with activation totals as equal as possible
+ * and renumber them so set g is the id range [g*S, (g+1)*S), S = E/n_groups.
+ * [SGLang] workload balancer: balancedness is mean/max of the per-rank load.
+ * Algorithm (the report gives none): experts in decreasing load (ties: lower
+ * id) each join the least-loaded set with room (ties: lower set); then, while
+ * the most and the least loaded sets differ, the swap between them whose load
+ * difference d (0 < d < gap) is closest to gap/2 is made (ties: lower ids);
+ * ids inside a set ascend with the logical id.
+ *   load  (E) int64 host, >= 0: activation counts (e.g. summed moe_layout counts).
+ *   phys_of_logical (E) int32 host out.
+ * Returns MOE_ERR_INVALID_ARG for E outside [1, 1024], n_groups not dividing
+ * E, a negative load or null pointers.
+ */
+moe_status_t moe_eplb_place(const int64_t* load, int E, int n_groups, int32_t* phys_of_logical);
+
 size_t moe_layout_workspace_bytes(int B, int K, int E);
 moe_status_t moe_layout(const int32_t* topk_ids, int B, int K, int E, int e_begin, int e_end,
                         int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,

@@ -123,3 +123,24 @@ def test_masked_entry_points_reject():
     assert L.moe_grouped_ffn_masked(p, None, p, 4, 16, 100, 128, 1, p, p, p, None, None, None, 1,
                                     p, 1, p, 1 << 30, 0, None) == m.MOE_ERR_INVALID_ARG
     assert "multiples of 64" in L.moe_last_error().decode()
+
+
+def test_eplb_place_matches_oracle_and_rejects():
+    """The library's host placement is the oracle's reading, id for id."""
+    import numpy as np
+    from oracle import eplb
+    rng = np.random.default_rng(7)
+    for E, G in [(8, 2), (16, 4), (256, 8), (12, 3), (64, 64), (40, 1), (1024, 8)]:
+        for _ in range(5):
+            load = rng.integers(0, 2000, size=E) * rng.integers(0, 2, size=E)   # with zero loads and ties
+            got = m.moe_eplb_place(load, G).numpy()
+            np.testing.assert_array_equal(got, eplb.balanced_placement(load, G))
+    L = m.lib()
+    buf = (ctypes.c_int64 * 10)(*range(10))
+    out = (ctypes.c_int32 * 10)()
+    P = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert L.moe_eplb_place(P(buf), 10, 3, P(out)) == m.MOE_ERR_INVALID_ARG
+    assert "divide" in L.moe_last_error().decode()
+    buf[4] = -1
+    assert L.moe_eplb_place(P(buf), 10, 2, P(out)) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_route_mapped(None, 4, 8, 2, None, None, None, None) == m.MOE_ERR_INVALID_ARG
