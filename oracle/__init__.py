@@ -18,6 +18,8 @@ Sources (cited by title and section in each function):
 Parity status of each function (what pins it, in tests/test_oracle_*.py):
   route          pinned: worked rows, closed-form two-way gates, full softmax
                  at K = E, brute-force top-K over {-1,0,1}^E.
+  route_shared   pinned: the layer with a shared expert equals the routed
+                 layer plus a dense SwiGLU of the shared weights per token.
   layout         pinned: brute-force construction, sum of counts, bijection.
   layout_masked  pinned: agrees with the contiguous layout (a different
                  construction) shifted to fixed row blocks; overflow keeps the
@@ -33,8 +35,8 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   both sides implement); its properties are checked.
 """
 from . import eplb, numerics
-from .moe import (route, layout, layout_masked, dispatch, silu, expert_ffn, grouped_ffn,
+from .moe import (route, route_shared, layout, layout_masked, dispatch, silu, expert_ffn, grouped_ffn,
                   grouped_ffn_masked, combine, layer)
 
-__all__ = ["eplb", "numerics", "route", "layout", "layout_masked", "dispatch", "silu", "expert_ffn",
+__all__ = ["eplb", "numerics", "route", "route_shared", "layout", "layout_masked", "dispatch", "silu", "expert_ffn",
            "grouped_ffn", "grouped_ffn_masked", "combine", "layer"]

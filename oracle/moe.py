@@ -70,6 +70,24 @@ def route(logits, K: int):
 # ----------------------------------------------------------------------------
 # layout
 # ----------------------------------------------------------------------------
+def route_shared(logits, K: int, n_shared: int):
+    """Routing with n_shared always-on (shared) experts.
+
+    Moreh report, "Overview": besides the routed experts, a shared expert runs
+    for every token regardless of routing; its section on library
+    optimisations merges the shared expert's GEMMs with others (horizontal
+    fusion).  Reading: the shared experts are experts E, E+1, ... that every
+    token selects with gate 1 (their output is added unweighted), appended
+    after the K routed slots, so the rest of the layer runs them as ordinary
+    expert groups.  Returns ids (T, K + n_shared), gates (T, K + n_shared).
+    """
+    ids, gates = route(logits, K)
+    T, E = np.asarray(logits).shape
+    extra = np.tile(np.arange(E, E + n_shared, dtype=np.int32), (T, 1))
+    return (np.concatenate([ids, extra], axis=1).astype(np.int32),
+            np.concatenate([gates, np.ones((T, n_shared))], axis=1))
+
+
 def layout(ids, E: int, e_begin: int, e_end: int, cap: int):
     """Per-expert counts, offsets and the (token, slot) <-> row permutation.
 
@@ -257,15 +275,23 @@ def combine(y, row_of, gates, out_dtype: str):
 # whole layer
 # ----------------------------------------------------------------------------
 def layer(x, logits, K, E, e_begin, e_end, weights_of, act, y_dtype, out_dtype,
-          gates_dtype="f32"):
+          gates_dtype="f32", n_shared=0):
     """route -> layout -> dispatch -> grouped FFN -> combine on one GPU's share.
 
     x (T, H) token rows (values on their storage grid), logits (T, E).
     weights_of(e) gives local expert e's dequantised weights.  Gates are
     stored as fp32 before use (gates_dtype) as the layer hands them between
-    steps in fp32.  Returns a dict with every intermediate.
+    steps in fp32.  With n_shared > 0 the shared experts E.. are appended to
+    the routing (route_shared) and to the local range, which must then end
+    at E.  Returns a dict with every intermediate.
     """
-    ids, gates = route(logits, K)
+    if n_shared:
+        if e_end != E:
+            raise ValueError("shared experts need the local range to end at E")
+        ids, gates = route_shared(logits, K, n_shared)
+        K, E, e_end = K + n_shared, E + n_shared, E + n_shared
+    else:
+        ids, gates = route(logits, K)
     gates_s = nx.round_act(gates, gates_dtype)
     T = np.asarray(x).shape[0]
     lay = layout(ids, E, e_begin, e_end, T * K)

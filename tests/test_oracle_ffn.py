@@ -105,3 +105,28 @@ def test_layer_local_range_offsets_expert_index():
             if e0 <= e < e1:
                 acc += np.float32(res["gates"][t, k]) * oracle.expert_ffn(x[t:t + 1], *Ws[e], "f32", "f32")[0]
         np.testing.assert_allclose(res["out"][t], acc, rtol=1e-6, atol=1e-6)
+
+
+def test_shared_expert_layer_is_routed_layer_plus_dense_ffn():
+    """With one shared expert (every token, gate 1) the layer's output is the
+    routed layer's output plus a dense SwiGLU of the shared weights on every
+    token -- the latter written with torch's F.linear / F.silu, not the
+    oracle's expert code."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(21)
+    T, E, K, H, I = 11, 6, 2, 16, 12
+    x = rng.standard_normal((T, H))
+    logits = rng.standard_normal((T, E))
+    W = [tuple(rng.standard_normal(s) / np.sqrt(s[1]) for s in ((I, H), (I, H), (H, I))) for _ in range(E + 1)]
+    routed = oracle.layer(x, logits, K, E, 0, E, lambda e: W[e], "f32", "f32", "f32")
+    shared = oracle.layer(x, logits, K, E, 0, E, lambda e: W[e], "f32", "f32", "f32", n_shared=1)
+    xt = torch.from_numpy(x)
+    g, u, d = (torch.from_numpy(m) for m in W[E])
+    dense = F.linear(F.silu(F.linear(xt, g)) * F.linear(xt, u), d).numpy()
+    np.testing.assert_allclose(shared["out"], routed["out"] + dense, rtol=1e-5, atol=1e-5)
+    ids, gates = oracle.route_shared(logits, K, 1)
+    assert (ids[:, K] == E).all() and (gates[:, K] == 1.0).all()
+    r_ids, r_g = oracle.route(logits, K)
+    np.testing.assert_array_equal(ids[:, :K], r_ids)
+    np.testing.assert_array_equal(gates[:, :K], r_g)
