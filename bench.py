@@ -51,6 +51,8 @@ def parse():
                     help="masked layout: rows per expert block (default T, nothing dropped)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step as a HIP graph and time its replays")
+    ap.add_argument("--shared-experts", type=int, default=0,
+                    help="always-on shared experts run in the same grouped FFN (all experts local)")
     ap.add_argument("--eplb", action="store_true",
                     help="balanced expert placement from 8 calibration batches (EP-share workloads)")
     return ap.parse_args()
@@ -59,8 +61,8 @@ def parse():
 # ----------------------------------------------------------------------------
 # algorithmic work per stage (what the method must move / compute)
 # ----------------------------------------------------------------------------
-def stage_work(cfg, counts_local, tokens_with_local):
-    T, E, K, H, I = cfg.T, cfg.E, cfg.K, cfg.H, cfg.I
+def stage_work(cfg, counts_local, tokens_with_local, K_slots=None):
+    T, E, K, H, I = cfg.T, cfg.E, cfg.K if K_slots is None else K_slots, cfg.H, cfg.I
     R = int(counts_local.sum())
     touched = int((counts_local > 0).sum())
     sx, sa, sw, sy, so = (ESIZE[cfg.x_dtype], ESIZE[cfg.act_dtype], ESIZE[cfg.w_dtype],
@@ -73,7 +75,7 @@ def stage_work(cfg, counts_local, tokens_with_local):
     sc_wd = touched * H * nbI * 4 if cfg.w_dtype == "fp8" else 0
     w = {
         "route": dict(bytes=T * E * 4 + T * K * 8, flops=0),
-        "layout": dict(bytes=T * K * 4 * 3 + cfg.cap * 4 + E * 4 * 2, flops=0),
+        "layout": dict(bytes=T * K * 4 * 3 + T * K * 4 + E * 4 * 2, flops=0),
         "dispatch": dict(bytes=tokens_with_local * H * sx + R * H * sa + sc_x, flops=0),
         "ffn_gate_up": dict(bytes=touched * 2 * I * H * sw + sc_wgu + R * H * sa + sc_x
                             + R * I * sa + sc_h, flops=4 * R * H * I),
@@ -287,6 +289,11 @@ def main():
     if a.eplb:
         placement = eplb_placement(m, cfg, dev)
         W = wl.gen_expert_weights(cfg, device=dev, experts=placement["local_logical"])
+    elif a.shared_experts:
+        if cfg.e_end != cfg.E:
+            raise SystemExit("--shared-experts needs the local range to end at E")
+        W = wl.gen_expert_weights(cfg, device=dev,
+                                  experts=list(range(cfg.e_begin, cfg.E + a.shared_experts)))
     else:
         W = wl.gen_expert_weights(cfg, device=dev)
     wdict = {"gate": W.gate, "up": W.up, "down": W.down}
@@ -294,7 +301,7 @@ def main():
         wdict.update(gate_scale=W.gate_scale, up_scale=W.up_scale, down_scale=W.down_scale)
     layer = m.MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end,
                        cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=dev, layout=a.layout,
-                       cap_per_expert=(a.cap_per_expert or None))
+                       cap_per_expert=(a.cap_per_expert or None), n_shared=a.shared_experts)
     if placement is not None:
         layer.expert_map = placement["map"]
     stages = layer.stages(x, logits, wdict)
@@ -303,19 +310,22 @@ def main():
     layer.forward(x, logits, wdict)
     torch.cuda.synchronize()
     import oracle
-    ids, _ = oracle.route(logits_cpu.numpy(), cfg.K)
+    if a.shared_experts:
+        ids, _ = oracle.route_shared(logits_cpu.numpy(), cfg.K, a.shared_experts)
+    else:
+        ids, _ = oracle.route(logits_cpu.numpy(), cfg.K)
     if placement is not None:
         ids = placement["phys"][ids]
-    lay = oracle.layout(ids, cfg.E, cfg.e_begin, cfg.e_end, cfg.cap)
+    lay = oracle.layout(ids, layer.E, layer.e_begin, layer.e_end, layer.cap)
     ref_row_of = (oracle.layout_masked(ids, cfg.E, cfg.e_begin, cfg.e_end, layer.cap_e)["row_of"]
                   if layer.masked else lay["row_of"])
     if not (np.array_equal(layer.topk_ids.cpu().numpy(), ids)
             and np.array_equal(layer.row_of.cpu().numpy(), ref_row_of)):
         print(json.dumps({"error": "parity gate failed: routing/layout differ from the oracle"}))
         sys.exit(1)
-    counts_local = lay["counts"][cfg.e_begin:cfg.e_end]
-    local = (ids >= cfg.e_begin) & (ids < cfg.e_end)
-    work, R, touched = stage_work(cfg, counts_local, int(local.any(axis=1).sum()))
+    counts_local = lay["counts"][layer.e_begin:layer.e_end]
+    local = (ids >= layer.e_begin) & (ids < layer.e_end)
+    work, R, touched = stage_work(cfg, counts_local, int(local.any(axis=1).sum()), layer.K)
 
     copy_gbs = measured_copy_gbs(dev)
     stream = torch.cuda.current_stream()
@@ -388,6 +398,8 @@ def main():
     }
     if a.layout == "masked":
         res["config"]["layout"] = {"kind": "masked", "cap_per_expert": layer.cap_e}
+    if a.shared_experts:
+        res["config"]["shared_experts"] = a.shared_experts
     if placement is not None:
         res["config"]["placement"] = "balanced (8 calibration batches)"
         res["eplb"] = eplb_report(m, cfg, logits, placement, layer)

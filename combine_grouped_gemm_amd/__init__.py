@@ -20,7 +20,7 @@ __all__ = ["MoeError", "lib", "library_path", "moe_version", "moe_route",
            "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
            "moe_ffn_workspace_bytes", "moe_ffn_gate_up", "moe_ffn_down",
            "moe_grouped_ffn", "moe_combine", "moe_layout_masked", "moe_ffn_gate_up_masked",
-           "moe_ffn_down_masked", "moe_grouped_ffn_masked", "moe_route_mapped", "moe_eplb_place",
+           "moe_ffn_down_masked", "moe_grouped_ffn_masked", "moe_route_mapped", "moe_eplb_place", "moe_route_shared",
            "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
            "MoELayer"]
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "moe_layout_masked": ([P, I, I, I, I, I, P, P, P, P, I, P, Z, P], S),
         "moe_route_mapped": ([P, I, I, I, P, P, P, P], S),
         "moe_eplb_place": ([P, I, I, P], S),
+        "moe_route_shared": ([P, I, I, I, I, P, P, P], S),
     }
     # the masked FFN calls take (m, E_local, cap_per_expert) where the others take
     # (offsets, E_local, cap_rows): same argument types
@@ -160,6 +161,25 @@ def moe_route_mapped(logits, K: int, phys_of_logical, topk_ids=None, topk_w=None
     _dev(topk_w, "topk_w", torch.float32, 2)
     _check(lib().moe_route_mapped(_ptr(logits), B, E, K, _ptr(phys_of_logical), _ptr(topk_ids),
                                   _ptr(topk_w), _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_route_shared(logits, K: int, n_shared: int, topk_ids=None, topk_w=None, stream=None):
+    """moe_route plus n_shared always-on experts: ids / gates (B, K + n_shared),
+    the last n_shared columns E, E+1, ... with gate 1."""
+    _dev(logits, "logits", torch.float32, 2)
+    B, E = logits.shape
+    Kt = K + n_shared
+    if topk_ids is None:
+        topk_ids = torch.empty((B, Kt), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((B, Kt), dtype=torch.float32, device=logits.device)
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    _dev(topk_w, "topk_w", torch.float32, 2)
+    if topk_ids.shape != (B, Kt) or topk_w.shape != (B, Kt):
+        raise ValueError(f"outputs must be ({B}, {Kt})")
+    _check(lib().moe_route_shared(_ptr(logits), B, E, K, int(n_shared), _ptr(topk_ids), _ptr(topk_w),
+                                  _stream(stream)))
     return topk_ids, topk_w
 
 

@@ -216,7 +216,7 @@ moe_status_t moe_route(const float* logits, int B, int E, int K, int32_t* topk_i
     moe_status_t s = check_route_shape(B, E, K);
     if (s != MOE_OK) return s;
     if (B > 0) REQUIRE(logits && topk_ids && topk_w, "null pointer argument");
-    return launched(moeep::launch_route(logits, B, E, K, topk_ids, topk_w, nullptr, stream), "moe_route");
+    return launched(moeep::launch_route(logits, B, E, K, topk_ids, topk_w, nullptr, 0, stream), "moe_route");
 }
 
 moe_status_t moe_route_mapped(const float* logits, int B, int E, int K, const int32_t* phys_of_logical,
@@ -225,8 +225,19 @@ moe_status_t moe_route_mapped(const float* logits, int B, int E, int K, const in
     if (s != MOE_OK) return s;
     REQUIRE(phys_of_logical, "null phys_of_logical");
     if (B > 0) REQUIRE(logits && topk_ids && topk_w, "null pointer argument");
-    return launched(moeep::launch_route(logits, B, E, K, topk_ids, topk_w, phys_of_logical, stream),
+    return launched(moeep::launch_route(logits, B, E, K, topk_ids, topk_w, phys_of_logical, 0, stream),
                     "moe_route_mapped");
+}
+
+moe_status_t moe_route_shared(const float* logits, int B, int E, int K, int n_shared, int32_t* ids,
+                              float* w, hipStream_t stream) {
+    moe_status_t s = check_route_shape(B, E, K);
+    if (s != MOE_OK) return s;
+    REQUIRE(n_shared >= 0 && E + n_shared <= 1024, "need 0 <= n_shared and E + n_shared <= 1024");
+    REQUIRE((long long)B * (K + n_shared) <= 0x7fffffffLL, "B*(K+n_shared) must fit in int32");
+    if (B > 0) REQUIRE(logits && ids && w, "null pointer argument");
+    return launched(moeep::launch_route(logits, B, E, K, ids, w, nullptr, n_shared, stream),
+                    "moe_route_shared");
 }
 
 moe_status_t moe_eplb_place(const int64_t* load, int E, int n_groups, int32_t* phys_of_logical) {

@@ -9,9 +9,10 @@
 
 namespace moeep {
 
-// route.hip (map: optional (E) device table logical -> physical expert id)
+// route.hip (map: optional (E) device table logical -> physical expert id; n_shared
+// always-on slots appended to each output row, ids E.., gate 1)
 hipError_t launch_route(const float* logits, int B, int E, int K, int32_t* ids, float* w,
-                        const int32_t* map, hipStream_t stream);
+                        const int32_t* map, int n_shared, hipStream_t stream);
 
 // placement.hip (host): balanced equal-size expert groups, see the file header
 bool place_experts(const int64_t* load, int E, int G, int32_t* phys_of_logical);

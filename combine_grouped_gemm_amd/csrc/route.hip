@@ -12,7 +12,9 @@
 // values with fp32 expf, written coalesced at the end.  With a placement map
 // (Moreh report, load balancing between GPUs: the router emits the renumbered
 // expert ids) the chosen ids are written through it; selection and gates are
-// unchanged.
+// unchanged.  With n_shared always-on experts (Moreh report, "Overview": a
+// shared expert runs for every token regardless of routing) each output row
+// gets n_shared more slots, ids E, E+1, ... with gate 1.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -41,7 +43,7 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 template <int EPL>
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const float* __restrict__ logits, int B, int E, int K, int32_t* __restrict__ ids,
-    float* __restrict__ w, const int32_t* __restrict__ map) {
+    float* __restrict__ w, const int32_t* __restrict__ map, int n_shared) {
     // dynamic LDS: per wave K gate numerators, then per wave K ids
     extern __shared__ char smem[];
     const int wave = threadIdx.x / kWave;
@@ -87,32 +89,35 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     const float inv = 1.0f / sum;
-    for (int k = lane; k < K; k += kWave) {
-        ids[(size_t)t * K + k] = map != nullptr ? map[s_id[k]] : s_id[k];
-        w[(size_t)t * K + k] = s_val[k] * inv;
+    const int ld = K + n_shared;                       // output row length
+    for (int k = lane; k < ld; k += kWave) {
+        const bool routed = k < K;
+        ids[(size_t)t * ld + k] = routed ? (map != nullptr ? map[s_id[k]] : s_id[k]) : E + (k - K);
+        w[(size_t)t * ld + k] = routed ? s_val[k] * inv : 1.0f;
     }
 }
 
 template <int EPL>
 hipError_t launch_epl(const float* logits, int B, int E, int K, int32_t* ids, float* w,
-                      const int32_t* map, hipStream_t stream) {
+                      const int32_t* map, int n_shared, hipStream_t stream) {
     dim3 grid((B + kRouteWaves - 1) / kRouteWaves), block(kRouteWaves * kWave);
     const size_t lds = (size_t)kRouteWaves * K * (sizeof(float) + sizeof(int));
-    hipLaunchKernelGGL(route_kernel<EPL>, grid, block, lds, stream, logits, B, E, K, ids, w, map);
+    hipLaunchKernelGGL(route_kernel<EPL>, grid, block, lds, stream, logits, B, E, K, ids, w, map,
+                       n_shared);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, int B, int E, int K, int32_t* ids, float* w,
-                        const int32_t* map, hipStream_t stream) {
+                        const int32_t* map, int n_shared, hipStream_t stream) {
     if (B == 0) return hipSuccess;
     const int epl = (E + kWave - 1) / kWave;
-    if (epl <= 1) return launch_epl<1>(logits, B, E, K, ids, w, map, stream);
-    if (epl <= 2) return launch_epl<2>(logits, B, E, K, ids, w, map, stream);
-    if (epl <= 4) return launch_epl<4>(logits, B, E, K, ids, w, map, stream);
-    if (epl <= 8) return launch_epl<8>(logits, B, E, K, ids, w, map, stream);
-    return launch_epl<16>(logits, B, E, K, ids, w, map, stream);
+    if (epl <= 1) return launch_epl<1>(logits, B, E, K, ids, w, map, n_shared, stream);
+    if (epl <= 2) return launch_epl<2>(logits, B, E, K, ids, w, map, n_shared, stream);
+    if (epl <= 4) return launch_epl<4>(logits, B, E, K, ids, w, map, n_shared, stream);
+    if (epl <= 8) return launch_epl<8>(logits, B, E, K, ids, w, map, n_shared, stream);
+    return launch_epl<16>(logits, B, E, K, ids, w, map, n_shared, stream);
 }
 
 }  // namespace moeep

@@ -14,7 +14,7 @@ import torch
 
 from . import (FP8_BLOCK, moe_combine, moe_dispatch, moe_ffn_down, moe_ffn_gate_up,
                moe_layout, moe_layout_masked, moe_layout_workspace_bytes, moe_route,
-               moe_route_mapped)
+               moe_route_mapped, moe_route_shared)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
@@ -29,12 +29,21 @@ class MoELayer:
     layout: 'contiguous' (rows of the local experts back to back, cap_rows
     rows, default T*K) or 'masked' (a fixed block of cap_per_expert rows per
     local expert, default T -- no slot can be dropped).
+    n_shared: always-on shared experts (every token, gate 1), run as experts
+    E, E+1, ... of the same grouped FFN; the local range must end at E and the
+    weights hold the shared experts after the routed ones.  self.E, self.K
+    and self.e_end then count them (self.E_routed, self.K_routed do not).
     """
 
     def __init__(self, seg_rows, E, K, H, I, e_begin, e_end, act_dtype, y_dtype, out_dtype,
-                 device="cuda", cap_rows=None, layout="contiguous", cap_per_expert=None):
+                 device="cuda", cap_rows=None, layout="contiguous", cap_per_expert=None, n_shared=0):
         self.seg_rows = tuple(int(b) for b in seg_rows)
         self.T = sum(self.seg_rows)
+        self.n_shared = int(n_shared)
+        if self.n_shared and e_end != E:
+            raise ValueError("shared experts need the local range to end at E")
+        self.E_routed, self.K_routed = E, K
+        E, K, e_end = E + self.n_shared, K + self.n_shared, e_end + self.n_shared
         self.E, self.K, self.H, self.I = E, K, H, I
         self.e_begin, self.e_end = e_begin, e_end
         self.E_loc = e_end - e_begin
@@ -47,8 +56,8 @@ class MoELayer:
             self.cap = self.E_loc * self.cap_e
         else:
             self.cap = self.T * K if cap_rows is None else int(cap_rows)
-        # rows a local expert gets under balanced routing: the FFN tile-shape hint
-        self.expected_rows = max(1, (self.T * K) // E)
+        # rows a routed local expert gets under balanced routing: the FFN tile-shape hint
+        self.expected_rows = max(1, (self.T * self.K_routed) // self.E_routed)
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         T, cap = self.T, max(self.cap, 1)
@@ -74,7 +83,12 @@ class MoELayer:
 
     # individual stages (each one library call) ---------------------------------
     def route(self, logits, stream=None):
-        if self.expert_map is None:
+        if self.n_shared:
+            if self.expert_map is not None:
+                raise ValueError("a placement map with shared experts is not supported")
+            moe_route_shared(logits, self.K_routed, self.n_shared, self.topk_ids, self.topk_w,
+                             stream=stream)
+        elif self.expert_map is None:
             moe_route(logits, self.K, self.topk_ids, self.topk_w, stream=stream)
         else:
             moe_route_mapped(logits, self.K, self.expert_map, self.topk_ids, self.topk_w, stream=stream)

@@ -121,6 +121,24 @@ moe_status_t moe_route_mapped(const float* logits, int B, int E, int K, const in
                               int32_t* topk_ids, float* topk_w, hipStream_t stream);
 
 /*
+ * moe_route_shared -- moe_route plus n_shared always-on (shared) experts.
+ * [Moreh] "Overview": besides the routed experts a shared expert runs for
+ * every token regardless of routing; "Library optimizations": its GEMMs are
+ * merged with others (horizontal fusion).  Here the shared experts become
+ * ordinary groups of the same grouped FFN: every output row holds the K
+ * routed picks of moe_route (same ids, order and renormalised gates) followed
+ * by n_shared slots with ids E, E+1, ..., E+n_shared-1 and gate 1.0.
+ *   ids, w  (B, K + n_shared) int32 / fp32 out.
+ * Run the rest of the layer with E' = E + n_shared experts and K' = K +
+ * n_shared slots (the shared experts' weights after the routed ones): every
+ * token then lands in each shared expert's group, and combine adds the
+ * shared outputs with weight 1.
+ * Errors as for moe_route, plus n_shared < 0 or E + n_shared > 1024.
+ */
+moe_status_t moe_route_shared(const float* logits, int B, int E, int K, int n_shared, int32_t* ids,
+                              float* w, hipStream_t stream);
+
+/*
  * moe_eplb_place -- expert placement for load balancing (host function; no
  * GPU work).  [Moreh] load balancing between GPUs: group E experts into
  * n_groups sets of E/n_groups with activation totals as equal as possible

@@ -144,3 +144,12 @@ def test_eplb_place_matches_oracle_and_rejects():
     buf[4] = -1
     assert L.moe_eplb_place(P(buf), 10, 2, P(out)) == m.MOE_ERR_INVALID_ARG
     assert L.moe_route_mapped(None, 4, 8, 2, None, None, None, None) == m.MOE_ERR_INVALID_ARG
+
+
+def test_route_shared_rejects():
+    L = m.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.moe_route_shared(p, 4, 1000, 8, 30, p, p, None) == m.MOE_ERR_INVALID_ARG
+    assert "n_shared" in L.moe_last_error().decode()
+    assert L.moe_route_shared(p, 4, 16, 2, -1, p, p, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_route_shared(None, 0, 16, 2, 1, None, None, None) == m.MOE_OK

@@ -1,0 +1,61 @@
+"""GPU parity of the layer with always-on shared experts (Moreh report,
+"Overview": a shared expert runs for every token regardless of routing),
+run as extra groups of the same grouped FFN launch: routing ids and the
+layout exact, outputs within the layer's tolerance of the oracle."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from harness import assert_close, has_gpu, to_np
+from oracle import numerics as nx
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+C = wl.CONFIGS
+CASES = [
+    (C["toy"], 1),
+    (wl.scaled(C["dsv3_decode"], "decode_small", seg_rows=(40,), E=32, K=4, H=512, I=256), 1),
+    (wl.scaled(C["dsv3_prefill"], "prefill_small", seg_rows=(600,), E=8, K=2, H=384, I=320), 2),
+    (wl.scaled(C["gptoss_fp8"], "fp8_small", seg_rows=(300,), E=8, K=2, H=320, I=192), 1),
+]
+
+
+@pytest.mark.parametrize("cfg,ns", CASES, ids=[f"{c.name}-shared{n}" for c, n in CASES])
+def test_layer_with_shared_experts(cfg, ns):
+    from combine_grouped_gemm_amd import MoELayer
+    print(f"[shared] {cfg.name} T={cfg.T} E={cfg.E}+{ns} K={cfg.K}+{ns}", flush=True)
+    x_cpu = wl.gen_x(cfg)
+    logits_cpu = wl.gen_logits(cfg, x_cpu)
+    W = wl.gen_expert_weights(cfg, device="cuda", experts=list(range(cfg.E + ns)))
+    w = {"gate": W.gate, "up": W.up, "down": W.down}
+    if cfg.w_dtype == "fp8":
+        w.update(gate_scale=W.gate_scale, up_scale=W.up_scale, down_scale=W.down_scale)
+    layer = MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, 0, cfg.E, cfg.act_dtype, cfg.y_dtype,
+                     cfg.out_dtype, n_shared=ns)
+    layer.forward([s.cuda() for s in x_cpu], logits_cpu.cuda(), w)
+    torch.cuda.synchronize()
+
+    def weights_of(j):
+        d = W.expert(j, "cpu")
+        if cfg.w_dtype == "fp8":
+            return tuple(nx.dequantize_fp8_blocks(to_np(d[k]), to_np(d[k + "_scale"]))
+                         for k in ("gate", "up", "down"))
+        return tuple(to_np(d[k]) for k in ("gate", "up", "down"))
+
+    x = np.concatenate([to_np(s) for s in x_cpu])
+    o = oracle.layer(x, logits_cpu.numpy(), cfg.K, cfg.E, 0, cfg.E, weights_of, cfg.act_dtype,
+                     cfg.y_dtype, cfg.out_dtype, n_shared=ns)
+    np.testing.assert_array_equal(layer.topk_ids.cpu().numpy(), o["ids"])
+    np.testing.assert_allclose(layer.topk_w.cpu().numpy(), o["gates"], rtol=1e-5, atol=1e-7)
+    np.testing.assert_array_equal(layer.offsets.cpu().numpy(), o["offsets"])
+    np.testing.assert_array_equal(layer.row_of.cpu().numpy(), o["row_of"])
+    R = int(o["offsets"][-1])
+    assert_close(to_np(layer.y[:R]), o["y"], cfg.act_dtype, "y")
+    assert_close(to_np(layer.out), o["out"], cfg.act_dtype, "out")
+    del layer, W
+    gc.collect()
+    torch.cuda.empty_cache()
