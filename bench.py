@@ -53,6 +53,8 @@ def parse():
                     help="also capture one step as a HIP graph and time its replays")
     ap.add_argument("--shared-experts", type=int, default=0,
                     help="always-on shared experts run in the same grouped FFN (all experts local)")
+    ap.add_argument("--micro-batches", type=int, default=1, choices=[1, 2],
+                    help="2: also time the two-micro-batch, two-stream schedule of the layer")
     ap.add_argument("--eplb", action="store_true",
                     help="balanced expert placement from 8 calibration batches (EP-share workloads)")
     return ap.parse_args()
@@ -168,6 +170,28 @@ def eplb_report(m, cfg, logits, placement, layer):
                 "balancedness": round(float(gl.mean() / gl.max()), 4)}
     return {"ranks": G, "contiguous_chunks": stats(before), "balanced_placement": stats(after),
             "calibration": "8 batches of the workload's size, other tokens, same router and bias"}
+
+
+def two_micro_batches(m, cfg, x, logits, wdict, layer, steps, warmup):
+    """Time the two-micro-batch, two-stream schedule (same inputs, same
+    per-token results: checked bit for bit against the single-batch run)."""
+    from combine_grouped_gemm_amd.layer import MicroBatchedLayer
+    ref = layer.forward(x, logits, wdict).clone()
+    mb = MicroBatchedLayer(cfg.seg_rows, layer.E_routed, layer.K_routed, cfg.H, cfg.I, cfg.e_begin,
+                           cfg.e_end, cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=ref.device)
+    oa, ob = mb.forward(x, logits, wdict)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(torch.cat([oa, ob]), ref))
+    for _ in range(warmup):
+        mb.forward(x, logits, wdict)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mb.forward(x, logits, wdict)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
+            "bitwise_equal_to_single_batch": same, "split": [mb.a.T, mb.b.T]}
 
 
 def graph_replay(layer, x, logits, wdict, steps, warmup):
@@ -405,6 +429,8 @@ def main():
         res["eplb"] = eplb_report(m, cfg, logits, placement, layer)
     if a.graph:
         res["graph_replay"] = graph_replay(layer, x, logits, wdict, a.steps, a.warmup)
+    if a.micro_batches == 2:
+        res["two_micro_batches"] = two_micro_batches(m, cfg, x, logits, wdict, layer, a.steps, a.warmup)
     if a.copy_calibration_mib:
         # one elementwise kernel that reads n*4 bytes and writes n*4 bytes
         n = a.copy_calibration_mib * (1 << 20) // 4

@@ -136,3 +136,75 @@ class MoELayer:
         for _, run in self.stages(x_segments, logits, w):
             run(stream)
         return self.out
+
+
+class MicroBatchedLayer:
+    """The layer over two micro-batches on two streams (Moreh report,
+    compute-communication overlapping: split the batch in two so one
+    micro-batch's dispatch/combine runs under the other's expert GEMMs).
+
+    The tokens are split at a segment boundary (or, for one segment, at its
+    middle row).  Stream 0 runs micro-batch A's six calls; stream 1 runs B's
+    route, layout and dispatch at once, starts B's GEMMs after A's, and B's
+    combine follows them, so A's combine overlaps B's GEMMs and B's dispatch
+    overlaps A's.  Per-token results equal the single-batch layer's bit for
+    bit (every row is computed by the same kernels in the same order).
+    Both streams have the default priority.
+    """
+
+    def __init__(self, seg_rows, *args, **kw):
+        seg_rows = [int(b) for b in seg_rows]
+        if len(seg_rows) > 1:
+            cut = len(seg_rows) // 2
+            self.parts = (seg_rows[:cut], seg_rows[cut:])
+        else:
+            half = seg_rows[0] // 2
+            self.parts = ([half], [seg_rows[0] - half])
+        if min(sum(p) for p in self.parts) < 1:
+            raise ValueError("each micro-batch needs at least one token")
+        self.a = MoELayer(self.parts[0], *args, **kw)
+        self.b = MoELayer(self.parts[1], *args, **kw)
+        self.T = self.a.T + self.b.T
+        # the whole batch's tile-shape hint, so both halves use the single-batch kernels
+        self.a.expected_rows = self.b.expected_rows = max(
+            1, (self.T * self.a.K_routed) // self.a.E_routed)
+        self.side = torch.cuda.Stream(device=self.a.out.device)   # default priority
+        self._ev_a_ffn = torch.cuda.Event()
+        self._ev_b_done = torch.cuda.Event()
+        self._ev_start = torch.cuda.Event()
+
+    def split_inputs(self, x_segments, logits):
+        """(x segments, logits) of each micro-batch, as views of the inputs."""
+        xs = list(x_segments)
+        Ta = self.a.T
+        if len(xs) > 1:
+            cut = len(self.parts[0])
+            xa, xb = xs[:cut], xs[cut:]
+        else:
+            xa, xb = [xs[0][:Ta]], [xs[0][Ta:]]
+        return (xa, logits[:Ta]), (xb, logits[Ta:])
+
+    def forward(self, x_segments, logits, w):
+        """Enqueue both micro-batches; returns (out_a, out_b) (token order: A then B)."""
+        (xa, la), (xb, lb) = self.split_inputs(x_segments, logits)
+        main = torch.cuda.current_stream()
+        self._ev_start.record(main)
+        self.side.wait_event(self._ev_start)
+        a, b = self.a, self.b
+        a.route(la, main)
+        a.layout(main)
+        a.dispatch(xa, main)
+        b.route(lb, self.side)
+        b.layout(self.side)
+        b.dispatch(xb, self.side)
+        a.gate_up(w, main)
+        a.down(w, main)
+        self._ev_a_ffn.record(main)
+        a.combine(main)
+        self.side.wait_event(self._ev_a_ffn)
+        b.gate_up(w, self.side)
+        b.down(w, self.side)
+        b.combine(self.side)
+        self._ev_b_done.record(self.side)
+        main.wait_event(self._ev_b_done)
+        return a.out, b.out

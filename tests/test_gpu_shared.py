@@ -59,3 +59,34 @@ def test_layer_with_shared_experts(cfg, ns):
     del layer, W
     gc.collect()
     torch.cuda.empty_cache()
+
+
+MB = [
+    wl.scaled(C["dsv3_prefill"], "prefill_small", seg_rows=(600,), E=8, K=2, H=384, I=320),
+    wl.scaled(C["ep8_share"], "ep_small", seg_rows=(100, 37, 64), E=16, K=3, H=256, I=128,
+              e_begin=4, e_end=10),
+]
+
+
+@pytest.mark.parametrize("cfg", MB, ids=[c.name for c in MB])
+def test_two_micro_batches_match_single_batch(cfg):
+    """Two micro-batches on two streams give the single-batch layer's output
+    bit for bit (Moreh report, compute-communication overlapping)."""
+    from combine_grouped_gemm_amd import MoELayer
+    from combine_grouped_gemm_amd.layer import MicroBatchedLayer
+    print(f"[micro-batches] {cfg.name} T={cfg.T}", flush=True)
+    x = [s.cuda() for s in wl.gen_x(cfg)]
+    logits = wl.gen_logits(cfg).cuda()
+    W = wl.gen_expert_weights(cfg, device="cuda")
+    w = {"gate": W.gate, "up": W.up, "down": W.down}
+    args = (cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end, cfg.act_dtype, cfg.y_dtype, cfg.out_dtype)
+    one = MoELayer(cfg.seg_rows, *args)
+    ref = one.forward(x, logits, w).clone()
+    two = MicroBatchedLayer(cfg.seg_rows, *args)
+    for _ in range(2):
+        oa, ob = two.forward(x, logits, w)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat([oa, ob]), ref)
+    del one, two, W
+    gc.collect()
+    torch.cuda.empty_cache()
