@@ -240,13 +240,17 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                     // row scales of the four output rows this lane holds
                     const float* as_row = s_as + (mrow + (lane >> 4) * 4) * nk + kstep;
                     const float asc[4] = {as_row[0], as_row[nk], as_row[2 * nk], as_row[3 * nk]};
+                    // all four products first, then their scaling: the MFMAs do
+                    // not wait for each other's consumers
+                    floatx4 part[FN];
 #pragma unroll
-                    for (int f = 0; f < FN; ++f) {
-                        const floatx4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    for (int f = 0; f < FN; ++f)
+                        part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[e], asc[e] * bsc[f], acc[i][f][e]);
-                    }
+                    for (int f = 0; f < FN; ++f)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[f][e], asc[e] * bsc[f], acc[i][f][e]);
                 }
             }
         };
