@@ -12,8 +12,7 @@
 // so each weight tile is streamed from HBM once.
 //
 // Scales: the tile's row scales and weight-column scales for every k-block
-// are copied to LDS once per tile with 4-byte direct loads (a row range of a
-// scale array is contiguous in global memory).  The MFMA v_mfma_f32_16x16x128_f8f6f4 yields the
+// are copied to LDS once per tile with 4-byte direct loads, k-block-major.  The MFMA v_mfma_f32_16x16x128_f8f6f4 yields the
 // unscaled block product from a zero accumulator; it is folded in as
 // acc += part * s_row * s_col.  Lane l feeds row (l % 16) with bytes
 // [32*(l/16), 32*(l/16)+32) of the block for both operands.
@@ -64,13 +63,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     __shared__ uint4 sb0[BN * CPR];
     __shared__ uint4 sa1[BM * CPR];
     __shared__ uint4 sb1[BN * CPR];
-    // scales: [tile row][k-block] and, per weight matrix, [weight row][k-block];
-    // a direct load writes 64 floats, so every array has one wave's worth of
-    // slack at its end (lanes past the end must not land in the next array)
-    constexpr int HALF = GATED ? BN / 2 : BN;        // weight rows per scale array
-    constexpr int BS_STRIDE = HALF * kMaxKBlocks + kWave;
-    __shared__ float s_as[kMaxKBlocks * BM + kWave];
-    __shared__ float s_bs[(GATED ? 2 : 1) * BS_STRIDE];
+    // scales, k-block-major: [k-block][tile row] and [k-block][tile weight row]
+    __shared__ __align__(16) float s_as[kMaxKBlocks * BM];
+    __shared__ float s_bs[kMaxKBlocks * BN];
     __shared__ int s_pre[kMaxExperts + 1];
     __shared__ int s_tmp[NT / kWave];
 
@@ -118,24 +113,26 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
         wide::wait_lgkm0();
         wide::block_barrier();
 
-        // ---- this tile's scales -> LDS with 4-byte direct loads; the row range of
-        // a scale array is contiguous in global memory and keeps its [row][k-block]
-        // layout in LDS.  Elements past the valid rows / columns re-read element 0.
+        // ---- this tile's scales -> LDS with 4-byte direct loads, transposed to
+        // k-block-major on the way (each load gathers 64 rows of one k-block), so
+        // a lane's four row scales are one 16-byte LDS read and the per-k-step
+        // offsets are immediates.  Rows / columns past the valid ones re-read
+        // element 0.
         {
+            // [k-block][row] in LDS: instruction q loads rows 64*(q % RB) .. of k-block q / RB
             const float* asrc = p.a_scales + (size_t)row0 * nk;
-            const int na = nvalid * nk;
-            for (int q0 = wave * kWave; q0 < BM * nk; q0 += NW * kWave) {
-                const int q = q0 + lane;
-                lds_dma4(asrc + (q < na ? q : 0), s_as + q0);
+            constexpr int RBA = BM / kWave, RBB = BN / kWave;
+            static_assert(BM % kWave == 0 && BN % kWave == 0, "scale staging by 64-row loads");
+            for (int q = wave; q < RBA * nk; q += NW) {
+                const int kb = q / RBA, r = (q - kb * RBA) * kWave + lane;
+                lds_dma4(asrc + (r < nvalid ? (size_t)r * nk + kb : 0), s_as + kb * BM + (q - kb * RBA) * kWave);
             }
-            const int nvc = N - col0 < HALF ? N - col0 : HALF;
-            for (int h = 0; h < (GATED ? 2 : 1); ++h) {
-                const float* bsrc = (h ? wus : wgs) + (size_t)col0 * nk;
-                const int nb = nvc * nk;
-                for (int q0 = wave * kWave; q0 < HALF * nk; q0 += NW * kWave) {
-                    const int q = q0 + lane;
-                    lds_dma4(bsrc + (q < nb ? q : 0), s_bs + h * BS_STRIDE + q0);
-                }
+            for (int q = wave; q < RBB * nk; q += NW) {
+                const int kb = q / RBB, c = (q - kb * RBB) * kWave + lane;      // tile weight row
+                const bool up = GATED && c >= BN / 2;
+                const int col = col0 + (up ? c - BN / 2 : c);
+                const float* bsrc = up ? wus : wgs;
+                lds_dma4(bsrc + (col < N ? (size_t)col * nk + kb : 0), s_bs + kb * BN + (q - kb * RBB) * kWave);
             }
         }
 
@@ -225,8 +222,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 const uint4 t1 = *reinterpret_cast<const uint4*>(bb + r * ROWB + wide::swz(r, c0 + 1) * 16);
                 bfr[f] = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
                                (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-                bsc[f] = (GATED && f >= FN / 2) ? s_bs[BS_STRIDE + (r - HALF) * nk + kstep]
-                                                : s_bs[r * nk + kstep];
+                bsc[f] = s_bs[kstep * BN + r];
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -238,8 +234,8 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                     const intx8 afr = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
                                             (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
                     // row scales of the four output rows this lane holds
-                    const float* as_row = s_as + (mrow + (lane >> 4) * 4) * nk + kstep;
-                    const float asc[4] = {as_row[0], as_row[nk], as_row[2 * nk], as_row[3 * nk]};
+                    const float4 as4 = *reinterpret_cast<const float4*>(s_as + kstep * BM + mrow + (lane >> 4) * 4);
+                    const float asc[4] = {as4.x, as4.y, as4.z, as4.w};
                     // all four products first, then their scaling: the MFMAs do
                     // not wait for each other's consumers
                     floatx4 part[FN];
