@@ -5,10 +5,12 @@ Test infrastructure only: nothing under ``oracle/`` is part of the product path.
 The formats themselves are not defined on the pages.  The SGLang "Expert
 Parallelism" page (backend table for MoE computation, the DeepGEMM row) names
 block-wise fp8 quantisation for the grouped GEMM; the convention used here
-(OCP e4m3fn, one fp32 scale per 1x128 block along the contraction dimension,
-scale = amax / 448, round to nearest even, saturate at +-448) is a reading that
-both sides implement, so its geometry is "parity unpinned" as far as the pages
-go.  The rounding helpers themselves are pinned against torch's CPU casts.
+(OCP e4m3fn, one fp32 scale per 1x128 block along the contraction dimension;
+for activations the scale is the smallest power of two s with amax / s <= 448,
+the E8M0 convention of the microscaling formats; round to nearest even,
+saturate at +-448) is a reading that both sides implement, so its geometry is
+"parity unpinned" as far as the pages go.  Weight scales are arbitrary fp32
+values given with the weights.  The rounding helpers themselves are pinned against torch's CPU casts.
 
 Every function rounds from exact fp64 values by the definition of a binary
 floating-point grid: scale the value so that one unit in the last place is 1,
@@ -54,14 +56,31 @@ def to_e4m3_sat(v) -> np.ndarray:
     return round_to_grid(c, E4M3_P, E4M3_EMIN)
 
 
+def block_scale_pow2(amax):
+    """The block scale for a block whose largest magnitude is amax (fp32):
+    the smallest power of two s = 2^e with amax <= 448 * s, e >= -127 (the
+    range of an E8M0 scale byte); s = 1 when amax = 0.  Written with an exact
+    frexp split, amax = m * 2^E with m in [0.5, 1): 448 = 0.875 * 2^9, so
+    e = E - 9 when m <= 0.875, else E - 8."""
+    amax = np.asarray(amax, dtype=np.float32)
+    out = np.ones(amax.shape, dtype=np.float32)
+    nz = amax > 0
+    m, E = np.frexp(amax[nz].astype(np.float64))
+    e = np.maximum(np.where(m <= 0.875, E - 9, E - 8), -127)
+    out[nz] = np.ldexp(1.0, e).astype(np.float32)
+    return out
+
+
 def quantize_fp8_blocks(v, block: int = FP8_BLOCK):
     """Block-wise fp8 quantisation along the last axis.
 
     For each run of ``block`` consecutive elements (the last run may be
-    shorter): amax = max |v|, s = amax / 448 in fp32 (s = 1 when amax = 0),
-    code = e4m3(v / s) with the division done in fp32, clamped to +-448 and
-    rounded to nearest even.  The arithmetic that decides each code is fp32,
-    the precision the kernels use for the same decision.
+    shorter): amax = max |v| in fp32, s = block_scale_pow2(amax) (the
+    smallest power of two with amax / s <= 448; 1 when amax = 0), code =
+    e4m3(v / s) with the division done in fp32 (exact: s is a power of two),
+    clamped to +-448 and rounded to nearest even.  A power-of-two scale is the
+    E8M0 convention of the microscaling formats; the matrix cores apply such a
+    scale themselves.
 
     Returns (codes, scales): codes are fp64 values on the e4m3 grid with the
     shape of ``v``; scales are fp32 with the last axis replaced by the number
@@ -75,8 +94,8 @@ def quantize_fp8_blocks(v, block: int = FP8_BLOCK):
     for b in range(nb):
         blk = v32[..., b * block:(b + 1) * block]
         amax = np.max(np.abs(blk), axis=-1)
-        s = np.where(amax == 0, np.float32(1.0), amax / np.float32(E4M3_MAX)).astype(np.float32)
-        with np.errstate(over="ignore"):
+        s = block_scale_pow2(amax)
+        with np.errstate(over="ignore", under="ignore"):
             ratio = (blk / s[..., None]).astype(np.float32)   # fp32 division
         codes[..., b * block:(b + 1) * block] = to_e4m3_sat(ratio.astype(np.float64))
         scales[..., b] = s

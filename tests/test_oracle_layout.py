@@ -136,9 +136,10 @@ def test_fp8_dispatch_copies_identical_codes():
             np.testing.assert_array_equal(xd[r], xd[rows[0]])
             np.testing.assert_array_equal(xs[r], xs[rows[0]])
         deq = oracle.numerics.dequantize_fp8_blocks(xd[rows[0]], xs[rows[0]])
-        # e4m3 keeps 3 fraction bits: relative error <= 2^-4 of the block max
+        # e4m3 keeps 3 fraction bits: error <= half a step of the top binade,
+        # 16 * s, with the power-of-two scale s < 2 * amax / 448
         amax = np.maximum(np.abs(x[t, :128]).max(), 1e-30)
-        assert np.max(np.abs(deq[:128] - x[t, :128])) <= amax / 448 * 16 * 1.0001
+        assert np.max(np.abs(deq[:128] - x[t, :128])) <= amax / 448 * 32 * 1.0001
 
 
 # ---------------------------------------------------------------------------
