@@ -58,6 +58,24 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
     return sign | (r - (120u << 3));              // rebias exponent 127 -> 7
 }
 
+// Activation block scale: the smallest power of two s = 2^e with
+// amax <= 448 * s and e >= -127 (an E8M0 scale byte's range); 1 for amax = 0.
+// With amax = m * 2^E, m in [0.5, 1) and 448 = 0.875 * 2^9: e = E - 9 when
+// m <= 0.875 (fraction bits <= 0x600000 in [1, 2) form), else E - 8.  Any
+// subnormal amax gets 2^-127.  The matrix cores apply such a scale exactly.
+__device__ __forceinline__ float pow2_block_scale(float amax) {
+    if (amax == 0.0f) return 1.0f;
+    const uint32_t u = __float_as_uint(amax);
+    if (u < 0x00800000u) return __uint_as_float(0x00400000u);     // 2^-127
+    const int E = (int)((u >> 23) & 0xffu) - 126;
+    int e = (u & 0x7fffffu) <= 0x600000u ? E - 9 : E - 8;
+    if (e < -127) e = -127;
+    return e == -127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+// E8M0 byte of a power-of-two scale from pow2_block_scale: its biased exponent.
+__device__ __forceinline__ int e8m0_of_pow2(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
+
 // ---------------------------------------------------------------------------
 // wave helpers
 // ---------------------------------------------------------------------------

@@ -64,12 +64,13 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
     if (!ok) return;
-    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+    const float s = pow2_block_scale(amax);
+    const float rs = 1.0f / s;               // exact: s is a power of two
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3_sat(f[i] / s) << (8 * i);
+    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3_sat(f[i] * rs) << (8 * i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3_sat(f[4 + i] / s) << (8 * i);
+    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3_sat(f[4 + i] * rs) << (8 * i);
     const int32_t* rows = row_of + (size_t)t * K;
     for (int k = 0; k < K; ++k) {
         const int r = rows[k];

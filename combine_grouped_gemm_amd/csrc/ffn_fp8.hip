@@ -17,8 +17,8 @@
 //
 // gate/up writes h as fp8: each tile covers exactly one 128-column block of
 // h per row, so the block amax is reduced inside the tile (16 lanes by xor
-// shuffles, then the waves of a row through LDS), s = amax / 448 and the
-// codes are written with the scale.
+// shuffles, then the waves of a row through LDS), s is the smallest power of
+// two with amax <= 448 s, and the codes are written with the scale.
 #include "gemm_wide_fp8.hpp"
 #include "grouped_tiles.hpp"
 
@@ -257,11 +257,12 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
                     float amax = 0.f;
 #pragma unroll
                     for (int w = 0; w < WNW; ++w) amax = fmaxf(amax, s_amax[w][r]);
-                    const float s = amax == 0.f ? 1.f : amax / 448.0f;
+                    const float s = pow2_block_scale(amax);
+                    const float rs = 1.0f / s;       // exact: s is a power of two
 #pragma unroll
                     for (int f = 0; f < FO; ++f) {
                         const int col = fcol(f) + (lane & 15);
-                        if (col < N) Out[(size_t)(row0 + r) * N + col] = (uint8_t)f32_to_e4m3_sat(hv[i][f][e] / s);
+                        if (col < N) Out[(size_t)(row0 + r) * N + col] = (uint8_t)f32_to_e4m3_sat(hv[i][f][e] * rs);
                     }
                     if (wn == 0 && (lane & 15) == 0) p.out_scales[(size_t)(row0 + r) * nbN + tc.nt] = s;
                 }

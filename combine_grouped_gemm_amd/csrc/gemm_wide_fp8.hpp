@@ -12,10 +12,14 @@
 // so each weight tile is streamed from HBM once.
 //
 // Scales: the tile's row scales and weight-column scales for every k-block
-// are copied to LDS once per tile with 4-byte direct loads, k-block-major.  The MFMA v_mfma_f32_16x16x128_f8f6f4 yields the
-// unscaled block product from a zero accumulator; it is folded in as
-// acc += part * s_row * s_col.  Lane l feeds row (l % 16) with bytes
-// [32*(l/16), 32*(l/16)+32) of the block for both operands.
+// are copied to LDS once per tile with 4-byte direct loads, k-block-major.
+// Row (activation) scales are powers of two, so the scaled MFMA
+// v_mfma_scale_f32_16x16x128_f8f6f4 applies them itself, exactly, as E8M0
+// bytes (lane l gives the scale of the row it feeds, l % 16, for its 32-byte
+// slice l / 16 of the block); the block product from a zero accumulator is
+// then folded in as acc += part * s_col with the weight column's fp32 scale.
+// Lane l feeds row (l % 16) with bytes [32*(l/16), 32*(l/16)+32) of the
+// block for both operands.
 //
 // K need not be a multiple of 128 (K = 2880 leaves a 64-byte tail block): in
 // the tail step the direct loads of chunks past K read a 16-byte zero block
@@ -233,20 +237,20 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                     const uint4 t1 = *reinterpret_cast<const uint4*>(ab + r * ROWB + wide::swz(r, c0 + 1) * 16);
                     const intx8 afr = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
                                             (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-                    // row scales of the four output rows this lane holds
-                    const float4 as4 = *reinterpret_cast<const float4*>(s_as + kstep * BM + mrow + (lane >> 4) * 4);
-                    const float asc[4] = {as4.x, as4.y, as4.z, as4.w};
-                    // all four products first, then their scaling: the MFMAs do
-                    // not wait for each other's consumers
+                    // the row scale (a power of two) of the A row this lane
+                    // feeds, as an E8M0 byte: the matrix core applies it
+                    const int sa8 = e8m0_of_pow2(s_as[kstep * BM + r]);
+                    // all four products first, then their column scaling: the
+                    // MFMAs do not wait for each other's consumers
                     floatx4 part[FN];
 #pragma unroll
                     for (int f = 0; f < FN; ++f)
                         part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                            afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, sa8, 0, 127);
 #pragma unroll
                     for (int f = 0; f < FN; ++f)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[f][e], asc[e] * bsc[f], acc[i][f][e]);
+                        for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[f][e], bsc[f], acc[i][f][e]);
                 }
             }
         };
@@ -314,11 +318,12 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                     float amax = 0.f;
 #pragma unroll
                     for (int w = 0; w < WNW; ++w) amax = fmaxf(amax, s_amax[w * BM + r]);
-                    const float s = amax == 0.f ? 1.f : amax / 448.0f;
+                    const float s = pow2_block_scale(amax);
+                    const float rs = 1.0f / s;       // exact: s is a power of two
 #pragma unroll
                     for (int f = 0; f < FO; ++f) {
                         const int col = fcol(f) + (lane & 15);
-                        if (col < N) Out[(size_t)(row0 + r) * N + col] = (uint8_t)f32_to_e4m3_sat(hv[i][f][e] / s);
+                        if (col < N) Out[(size_t)(row0 + r) * N + col] = (uint8_t)f32_to_e4m3_sat(hv[i][f][e] * rs);
                     }
                     if (wn == 0 && (lane & 15) == 0) p.out_scales[(size_t)(row0 + r) * nbN + tc.nt] = s;
                 }
