@@ -19,7 +19,7 @@
 namespace moeep {
 namespace {
 
-constexpr int kDispThreads = 256;      // one 16-byte source vector per thread
+constexpr int kDispThreads = 448;      // one 16-byte source vector per thread (7 waves: a 7168-element bf16 row is two blocks)
 
 __device__ __forceinline__ const void* token_row(const SegTable& seg, int t, size_t row_bytes) {
     int i = 0;

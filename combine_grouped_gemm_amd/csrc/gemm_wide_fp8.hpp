@@ -12,7 +12,8 @@
 // so each weight tile is streamed from HBM once.
 //
 // Scales: the tile's row scales and weight-column scales for every k-block
-// are copied to LDS once per tile with 4-byte direct loads, k-block-major.
+// are copied to LDS once per tile with 4-byte direct loads over contiguous
+// runs, row-major with a fixed row stride.
 // Row (activation) scales are powers of two, so the scaled MFMA
 // v_mfma_scale_f32_16x16x128_f8f6f4 applies them itself, exactly, as E8M0
 // bytes (lane l gives the scale of the row it feeds, l % 16, for its 32-byte
@@ -36,6 +37,7 @@ using wide::ic;
 constexpr int CPR = 8;              // 16-byte chunks per 128-byte row step
 constexpr int ROWB = 128;           // bytes per LDS row = fp8 elements per k-step
 constexpr int kMaxKBlocks = 23;     // scale blocks a tile keeps in LDS (K <= 2944)
+constexpr int SK = kMaxKBlocks;     // LDS row stride of the scale tables (odd: conflict-free)
 
 // source of the tail block's missing chunks
 __device__ __align__(16) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
@@ -55,21 +57,23 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     constexpr int A_BLOCKS = BM * CPR / 64;          // 1 KiB blocks of a row stage
     constexpr int B_BLOCKS = BN * CPR / 64;
     constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;
-    constexpr int LPS = (BLOCKS + NW - 1) / NW;      // direct loads per wave per stage (at most)
+    constexpr int LPS = BLOCKS / NW;                 // direct loads per wave per stage
     constexpr int FM = BM / 16 / WMW;
     constexpr int WN = BN / WNW;
     constexpr int FN = WN / 16;
     constexpr int BNO = GATED ? BN / 2 : BN;
     static_assert(BM % (16 * WMW) == 0 && BN % (16 * WNW) == 0 && (!GATED || (FN % 2 == 0 && BNO == 128)),
                   "tile shape");
+    static_assert(BLOCKS % NW == 0, "every wave issues LPS loads per stage");
+    static_assert(BM * SK % kWave == 0 && BN * SK % kWave == 0, "scale staging by 64-lane loads");
 
     __shared__ uint4 sa0[BM * CPR];
     __shared__ uint4 sb0[BN * CPR];
     __shared__ uint4 sa1[BM * CPR];
     __shared__ uint4 sb1[BN * CPR];
-    // scales, k-block-major: [k-block][tile row] and [k-block][tile weight row]
-    __shared__ __align__(16) float s_as[kMaxKBlocks * BM];
-    __shared__ float s_bs[kMaxKBlocks * BN];
+    // scales, row-major with row stride SK: [tile row][k-block], [tile weight row][k-block]
+    __shared__ float s_as[BM * SK];
+    __shared__ float s_bs[BN * SK];
     __shared__ int s_pre[kMaxExperts + 1];
     __shared__ int s_tmp[NT / kWave];
 
@@ -117,35 +121,33 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
         wide::wait_lgkm0();
         wide::block_barrier();
 
-        // ---- this tile's scales -> LDS with 4-byte direct loads, transposed to
-        // k-block-major on the way (each load gathers 64 rows of one k-block), so
-        // a lane's four row scales are one 16-byte LDS read and the per-k-step
-        // offsets are immediates.  Rows / columns past the valid ones re-read
-        // element 0.
+        // ---- this tile's scales -> LDS, row-major with a fixed row stride of
+        // SK = kMaxKBlocks floats ([tile row][k-block]; odd, so the 16 rows one
+        // MFMA operand touches fall into distinct banks).  Global scales are
+        // [row][k-block] with nk per row, so 4-byte direct loads over the flat
+        // index e = row * SK + k read one contiguous run per tile (a few cache
+        // lines per load); lanes with k >= nk or past the valid rows / columns
+        // re-read element 0, whose value no output uses.
         {
-            // [k-block][row] in LDS: instruction q loads rows 64*(q % RB) .. of k-block q / RB
             const float* asrc = p.a_scales + (size_t)row0 * nk;
-            constexpr int RBA = BM / kWave, RBB = BN / kWave;
-            static_assert(BM % kWave == 0 && BN % kWave == 0, "scale staging by 64-row loads");
-            for (int q = wave; q < RBA * nk; q += NW) {
-                const int kb = q / RBA, r = (q - kb * RBA) * kWave + lane;
-                lds_dma4(asrc + (r < nvalid ? (size_t)r * nk + kb : 0), s_as + kb * BM + (q - kb * RBA) * kWave);
+            for (int q = wave; q < BM * SK / kWave; q += NW) {
+                const int e = q * kWave + lane, r = e / SK, k = e - r * SK;
+                lds_dma4(asrc + (r < nvalid && k < nk ? r * nk + k : 0), s_as + q * kWave);
             }
-            for (int q = wave; q < RBB * nk; q += NW) {
-                const int kb = q / RBB, c = (q - kb * RBB) * kWave + lane;      // tile weight row
+            for (int q = wave; q < BN * SK / kWave; q += NW) {
+                const int e = q * kWave + lane, c = e / SK, k = e - c * SK;      // tile weight row c
                 const bool up = GATED && c >= BN / 2;
                 const int col = col0 + (up ? c - BN / 2 : c);
                 const float* bsrc = up ? wus : wgs;
-                lds_dma4(bsrc + (col < N ? (size_t)col * nk + kb : 0), s_bs + kb * BN + (q - kb * RBB) * kWave);
+                lds_dma4(bsrc + (col < N && k < nk ? (size_t)col * nk + k : 0), s_bs + q * kWave);
             }
         }
-
         const bool w_lines = Kdim % 128 == 0;
         // per-lane source offsets (32-bit, relative to the tile's first row or to
         // the expert's weight matrices).  Wave w loads the 1 KiB blocks w, w + NW, ...
         // of a stage (8 rows each; row blocks first, then weight blocks); rows /
-        // columns past the valid ones re-read row 0.  Every step waits for all
-        // loads, so waves may issue different numbers of them.
+        // columns past the valid ones re-read row 0.  Every wave issues LPS
+        // loads per stage.
         const char* abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
         const char* gbase = reinterpret_cast<const char*>(wg);
         const char* ubase = reinterpret_cast<const char*>(wu);
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 const uint4 t1 = *reinterpret_cast<const uint4*>(bb + r * ROWB + wide::swz(r, c0 + 1) * 16);
                 bfr[f] = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
                                (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-                bsc[f] = s_bs[kstep * BN + r];
+                bsc[f] = s_bs[r * SK + kstep];
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                                             (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
                     // the row scale (a power of two) of the A row this lane
                     // feeds, as an E8M0 byte: the matrix core applies it
-                    const int sa8 = e8m0_of_pow2(s_as[kstep * BM + r]);
+                    const int sa8 = e8m0_of_pow2(s_as[r * SK + kstep]);
                     // all four products first, then their column scaling: the
                     // MFMAs do not wait for each other's consumers
                     floatx4 part[FN];
