@@ -16,6 +16,7 @@ included unless --no-cpu-baseline is given.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -55,6 +56,9 @@ def parse():
                     help="always-on shared experts run in the same grouped FFN (all experts local)")
     ap.add_argument("--micro-batches", type=int, default=1, choices=[1, 2],
                     help="2: also time the two-micro-batch, two-stream schedule of the layer")
+    ap.add_argument("--w-scales", default="", choices=["", "fp32", "pow2"],
+                    help="fp8 weight block scales: any fp32 value or powers of two only "
+                         "(default: the workload's own)")
     ap.add_argument("--eplb", action="store_true",
                     help="balanced expert placement from 8 calibration batches (EP-share workloads)")
     return ap.parse_args()
@@ -302,6 +306,8 @@ def main():
     import combine_grouped_gemm_amd as m
     m.lib()                                     # loud failure if the HIP library is missing
     cfg = wl.CONFIGS[a.workload]
+    if a.w_scales:
+        cfg = dataclasses.replace(cfg, w_scales=a.w_scales)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
@@ -320,9 +326,7 @@ def main():
                                   experts=list(range(cfg.e_begin, cfg.E + a.shared_experts)))
     else:
         W = wl.gen_expert_weights(cfg, device=dev)
-    wdict = {"gate": W.gate, "up": W.up, "down": W.down}
-    if cfg.w_dtype == "fp8":
-        wdict.update(gate_scale=W.gate_scale, up_scale=W.up_scale, down_scale=W.down_scale)
+    wdict = W.as_dict()
     layer = m.MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end,
                        cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=dev, layout=a.layout,
                        cap_per_expert=(a.cap_per_expert or None), n_shared=a.shared_experts)
@@ -409,7 +413,8 @@ def main():
         "dtype": cfg.act_dtype, "data": "synthetic (seeded; random-init expert weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "K": cfg.K, "H": cfg.H, "I": cfg.I,
                    "local_experts": [cfg.e_begin, cfg.e_end], "segments": len(cfg.seg_rows),
-                   "rows": R, "experts_touched": touched},
+                   "rows": R, "experts_touched": touched,
+                   **({"weight_scales": cfg.w_scales} if cfg.w_dtype == "fp8" else {})},
         "roofline": roof,
         "grouped_ffn": {"ms": round(ffn_ms, 4), "TFLOP_s": round(ffn_flops / (ffn_ms / 1e3) / 1e12, 2),
                         "mfma_frac": round(ffn_flops / (ffn_ms / 1e3) / 1e12 / mfma_peak, 4),

@@ -21,11 +21,11 @@ __all__ = ["MoeError", "lib", "library_path", "moe_version", "moe_route",
            "moe_ffn_workspace_bytes", "moe_ffn_gate_up", "moe_ffn_down",
            "moe_grouped_ffn", "moe_combine", "moe_layout_masked", "moe_ffn_gate_up_masked",
            "moe_ffn_down_masked", "moe_grouped_ffn_masked", "moe_route_mapped", "moe_eplb_place", "moe_route_shared",
-           "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
+           "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_FP8_E4M3_PO2",
            "MoELayer"]
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP8_E4M3_PO2 = 0, 1, 2, 3
 FP8_BLOCK = 128
 MAX_SEGMENTS = 64
 
@@ -303,12 +303,22 @@ def _rows_arg(rows, cap_per_expert, E_loc, n_rows):
     return int(cap_per_expert)
 
 
+def _w_code(act, w_scales_pow2):
+    """Weight dtype code: fp8 weights whose block scales are all powers of two
+    are declared as MOE_FP8_E4M3_PO2."""
+    if w_scales_pow2 and act != MOE_FP8_E4M3:
+        raise ValueError("w_scales_pow2 applies to fp8 weights only")
+    return MOE_FP8_E4M3_PO2 if w_scales_pow2 else act
+
+
 def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_up_scales=None,
-                    h=None, h_scales=None, expected_rows=0, stream=None, cap_per_expert=None):
+                    h=None, h_scales=None, expected_rows=0, stream=None, cap_per_expert=None,
+                    w_scales_pow2=False):
     """h = silu(Xd Wg^T) * (Xd Wu^T) per local expert -> (cap_rows, I) [+ scales].
     expected_rows: rows a local expert is expected to get (tile-shape hint only).
     With cap_per_expert given, ``offsets`` is the masked layout's m and the call
-    is moe_ffn_gate_up_masked."""
+    is moe_ffn_gate_up_masked.  w_scales_pow2: the fp8 weight scales are all
+    powers of two (weight dtype MOE_FP8_E4M3_PO2)."""
     _dev(xd, "xd", ndim=2)
     _dev(w_gate, "w_gate", xd.dtype, 3)
     _dev(w_up, "w_up", xd.dtype, 3)
@@ -323,7 +333,7 @@ def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_
     fn = lib().moe_ffn_gate_up if cap_per_expert is None else lib().moe_ffn_gate_up_masked
     _check(fn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, third, H, I, act,
               _ptr(w_gate), _ptr(w_up), _ptr(w_gate_scales), _ptr(w_up_scales),
-              act, _ptr(h), _ptr(h_scales), int(expected_rows), _stream(stream)))
+              _w_code(act, w_scales_pow2), _ptr(h), _ptr(h_scales), int(expected_rows), _stream(stream)))
     return h, h_scales
 
 
@@ -332,9 +342,9 @@ def _y_dtype_for(act):
 
 
 def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dtype=None,
-                 expected_rows=0, stream=None, cap_per_expert=None):
-    """y = h Wd^T per local expert -> (cap_rows, H).  cap_per_expert: as in
-    moe_ffn_gate_up (moe_ffn_down_masked)."""
+                 expected_rows=0, stream=None, cap_per_expert=None, w_scales_pow2=False):
+    """y = h Wd^T per local expert -> (cap_rows, H).  cap_per_expert and
+    w_scales_pow2: as in moe_ffn_gate_up (moe_ffn_down_masked)."""
     _dev(h, "h", ndim=2)
     _dev(w_down, "w_down", h.dtype, 3)
     E_loc, H, I = _ffn_shapes(h, w_down, False)
@@ -346,16 +356,16 @@ def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dty
         y = torch.empty((cap, H), dtype=y_dtype, device=h.device)
     fn = lib().moe_ffn_down if cap_per_expert is None else lib().moe_ffn_down_masked
     _check(fn(_ptr(h), _ptr(h_scales), _ptr(offsets), E_loc, third, H, I, act,
-              _ptr(w_down), _ptr(w_down_scales), act, _ptr(y), _DT[y.dtype],
+              _ptr(w_down), _ptr(w_down_scales), _w_code(act, w_scales_pow2), _ptr(y), _DT[y.dtype],
               int(expected_rows), _stream(stream)))
     return y
 
 
 def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=None,
                     w_up_scales=None, w_down_scales=None, y=None, y_dtype=None, ws=None,
-                    expected_rows=0, stream=None, cap_per_expert=None):
-    """Both FFN stages with h held in the workspace ``ws``.  cap_per_expert:
-    as in moe_ffn_gate_up (moe_grouped_ffn_masked)."""
+                    expected_rows=0, stream=None, cap_per_expert=None, w_scales_pow2=False):
+    """Both FFN stages with h held in the workspace ``ws``.  cap_per_expert
+    and w_scales_pow2: as in moe_ffn_gate_up (moe_grouped_ffn_masked)."""
     _dev(xd, "xd", ndim=2)
     for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _dev(w, n, xd.dtype, 3)
@@ -372,7 +382,7 @@ def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=
     fn = lib().moe_grouped_ffn if cap_per_expert is None else lib().moe_grouped_ffn_masked
     _check(fn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, third, H, I, act,
               _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
-              _ptr(w_up_scales), _ptr(w_down_scales), act, _ptr(y),
+              _ptr(w_up_scales), _ptr(w_down_scales), _w_code(act, w_scales_pow2), _ptr(y),
               _DT[y.dtype], _ptr(ws), ws.numel() * ws.element_size(),
               int(expected_rows), _stream(stream)))
     return y

@@ -79,7 +79,7 @@ moe_status_t check_ffn_common(const void* a, Rows rows, int E_local, int cap_row
     REQUIRE((long long)cap_rows * (H > I ? H : I) <= 0x7fffffffLL * 4LL, "cap_rows * H too large");
     REQUIRE(aligned16(a), "activation pointer must be 16-byte aligned");
     const bool ok = (act_dt == MOE_F32 && w_dt == MOE_F32) || (act_dt == MOE_BF16 && w_dt == MOE_BF16) ||
-                    (act_dt == MOE_FP8_E4M3 && w_dt == MOE_FP8_E4M3);
+                    (act_dt == MOE_FP8_E4M3 && (w_dt == MOE_FP8_E4M3 || w_dt == MOE_FP8_E4M3_PO2));
     if (!ok) return fail(MOE_ERR_UNSUPPORTED, "unsupported (act_dt, w_dt) = (%d, %d)", act_dt, w_dt);
     return MOE_OK;
 }
@@ -94,8 +94,9 @@ moe_status_t check_y_dtype(moe_dtype_t act_dt, moe_dtype_t y_dt) {
 moeep::FfnArgs ffn_args(const void* a, const float* a_scales, Rows rows, int E_local,
                         int cap_rows, int Kdim, int N, const void* w0, const void* w1,
                         const float* w0s, const float* w1s, void* out, float* out_scales,
-                        int expected_rows) {
+                        int expected_rows, moe_dtype_t w_dt) {
     moeep::FfnArgs f;
+    f.w_scales_pow2 = w_dt == MOE_FP8_E4M3_PO2;
     f.a = a;
     f.a_scales = a_scales;
     f.offsets = rows.offsets;
@@ -147,7 +148,7 @@ moe_status_t ffn_gate_up(const void* xd, const float* xd_scales, Rows rows,
     if (act_dt == MOE_FP8_E4M3)
         REQUIRE(xd_scales && w_gate_scales && w_up_scales && h_scales, "fp8 needs all scale pointers");
     auto f = ffn_args(xd, xd_scales, rows, E_local, cap_rows, H, I, w_gate, w_up, w_gate_scales,
-                      w_up_scales, h, h_scales, expected_rows);
+                      w_up_scales, h, h_scales, expected_rows, w_dt);
     return launched(run_ffn(f, act_dt, true, stream), "ffn gate/up");
 }
 
@@ -163,7 +164,7 @@ moe_status_t ffn_down(const void* h, const float* h_scales, Rows rows, int E_loc
     REQUIRE(aligned16(w_down) && aligned16(y), "weights and y must be 16-byte aligned");
     if (act_dt == MOE_FP8_E4M3) REQUIRE(h_scales && w_down_scales, "fp8 needs all scale pointers");
     auto f = ffn_args(h, h_scales, rows, E_local, cap_rows, I, H, w_down, nullptr, w_down_scales,
-                      nullptr, y, nullptr, expected_rows);
+                      nullptr, y, nullptr, expected_rows, w_dt);
     return launched(run_ffn(f, act_dt, false, stream), "ffn down");
 }
 

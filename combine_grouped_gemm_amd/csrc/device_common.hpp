@@ -76,6 +76,24 @@ __device__ __forceinline__ float pow2_block_scale(float amax) {
 // E8M0 byte of a power-of-two scale from pow2_block_scale: its biased exponent.
 __device__ __forceinline__ int e8m0_of_pow2(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
 
+// 1 / s for s = 2^e, e in [-127, 127], exactly: the bits of 2^-e are
+// (127 - e) << 23 = 0x7f000000 - bits(s) for e in [-126, 126]; 2^-127 (the one
+// subnormal) and 2^127 are each other's reciprocal.
+__device__ __forceinline__ float pow2_recip(float s) {
+    const uint32_t u = __float_as_uint(s);
+    if (u < 0x00800000u) return __uint_as_float(0x7f000000u);
+    if (u >= 0x7f000000u) return __uint_as_float(0x00400000u);
+    return __uint_as_float(0x7f000000u - u);
+}
+
+// Two values with |v| <= 448 to OCP e4m3 codes (round to nearest even) by
+// the hardware conversion, first value in bits 7:0, second in bits 15:8.
+// Identical to f32_to_e4m3_sat on that range (checked exhaustively at every
+// code, rounding tie and its neighbours on gfx950).
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
 // ---------------------------------------------------------------------------
 // wave helpers
 // ---------------------------------------------------------------------------
@@ -102,6 +120,8 @@ __device__ __forceinline__ uint64_t match_mask(uint32_t key, uint64_t active, in
     return m;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware exponential and reciprocal
+// (about 1 ulp each; the result is rounded to bf16 or fp8 afterwards).
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 }  // namespace moeep

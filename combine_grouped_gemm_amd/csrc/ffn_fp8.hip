@@ -296,10 +296,10 @@ hipError_t launch_cfg(const FfnArgs& a, hipStream_t stream) {
                              stream, &per_cu);
 }
 
-template <bool GATED>
+template <bool GATED, bool PO2W>
 hipError_t launch_wide(const FfnArgs& a, hipStream_t stream) {
     static int per_cu = 0;
-    return launch_persistent(widefp8::grouped_gemm_fp8_wide_kernel<192, 256, 2, 4, GATED>, 512, a,
+    return launch_persistent(widefp8::grouped_gemm_fp8_wide_kernel<192, 256, 2, 4, GATED, PO2W>, 512, a,
                              stream, &per_cu);
 }
 
@@ -311,8 +311,11 @@ hipError_t launch_ffn_fp8(const FfnArgs& a, bool gated, hipStream_t stream) {
     const int nbK = (a.Kdim + 127) / 128;
     const bool wide_ok = nbK <= widefp8::kMaxKBlocks &&
                          (unsigned long long)a.N * a.Kdim < (1ull << 32);
-    if (wide_ok && a.rows_hint >= 48)
-        return gated ? launch_wide<true>(a, stream) : launch_wide<false>(a, stream);
+    if (wide_ok && a.rows_hint >= 48) {
+        if (a.w_scales_pow2)
+            return gated ? launch_wide<true, true>(a, stream) : launch_wide<false, true>(a, stream);
+        return gated ? launch_wide<true, false>(a, stream) : launch_wide<false, false>(a, stream);
+    }
     return gated ? launch_cfg<128, 256, 2, 4, true>(a, stream)
                  : launch_cfg<128, 128, 2, 2, false>(a, stream);
 }

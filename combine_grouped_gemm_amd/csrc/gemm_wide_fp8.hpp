@@ -17,8 +17,10 @@
 // Row (activation) scales are powers of two, so the scaled MFMA
 // v_mfma_scale_f32_16x16x128_f8f6f4 applies them itself, exactly, as E8M0
 // bytes (lane l gives the scale of the row it feeds, l % 16, for its 32-byte
-// slice l / 16 of the block); the block product from a zero accumulator is
-// then folded in as acc += part * s_col with the weight column's fp32 scale.
+// slice l / 16 of the block).  With arbitrary fp32 weight scales the block
+// product from a zero accumulator is folded in as acc += part * s_col; with
+// power-of-two weight scales (PO2W) the MFMA applies the column scale too and
+// accumulates in place, so the k-loop has no per-output vector arithmetic.
 // Lane l feeds row (l % 16) with bytes [32*(l/16), 32*(l/16)+32) of the
 // block for both operands.
 //
@@ -51,7 +53,7 @@ __device__ __forceinline__ void lds_dma4(const void* g, void* lds_wave_base) {
 
 // Waves laid out WMW (rows) x WNW (weight rows); a wave owns the interleaved
 // 16-row fragments {wm, wm + WMW, ...} and BN / WNW weight rows.
-template <int BM, int BN, int WMW, int WNW, bool GATED>
+template <int BM, int BN, int WMW, int WNW, bool GATED, bool PO2W>
 __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kernel(FfnArgs p) {
     constexpr int NT = 64 * WMW * WNW, NW = WMW * WNW;
     constexpr int A_BLOCKS = BM * CPR / 64;          // 1 KiB blocks of a row stage
@@ -230,6 +232,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                                (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
                 bsc[f] = s_bs[r * SK + kstep];
             }
+            int sb8[FN];        // weight-row scales as E8M0 bytes (power-of-two weight scales)
+#pragma unroll
+            for (int f = 0; f < FN; ++f) sb8[f] = PO2W ? e8m0_of_pow2(bsc[f]) : 127;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int mrow = (wm + WMW * i) * 16;
@@ -242,17 +247,25 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                     // the row scale (a power of two) of the A row this lane
                     // feeds, as an E8M0 byte: the matrix core applies it
                     const int sa8 = e8m0_of_pow2(s_as[r * SK + kstep]);
-                    // all four products first, then their column scaling: the
-                    // MFMAs do not wait for each other's consumers
-                    floatx4 part[FN];
+                    if constexpr (PO2W) {
+                        // both scales in the matrix core: accumulate in place
 #pragma unroll
-                    for (int f = 0; f < FN; ++f)
-                        part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, sa8, 0, 127);
+                        for (int f = 0; f < FN; ++f)
+                            acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                afr, bfr[f], acc[i][f], 0, 0, 0, sa8, 0, sb8[f]);
+                    } else {
+                        // all four products first, then their column scaling:
+                        // the MFMAs do not wait for each other's consumers
+                        floatx4 part[FN];
 #pragma unroll
-                    for (int f = 0; f < FN; ++f)
+                        for (int f = 0; f < FN; ++f)
+                            part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, sa8, 0, 127);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[f][e], bsc[f], acc[i][f][e]);
+                        for (int f = 0; f < FN; ++f)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[f][e], bsc[f], acc[i][f][e]);
+                    }
                 }
             }
         };
@@ -279,7 +292,12 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             // row amax over 16 lanes (shuffles) and the 4 column waves, through
             // the row stage the last k-step did not read (every wave has passed
             // the barrier after its last read, and no load is in flight)
-            float* s_amax = reinterpret_cast<float*>(((nk - 1) & 1) ? sa0 : sa1);
+            float* s_amax = reinterpret_cast<float*>(((nk - 1) & 1) ? sb0 : sb1);
+            // the h tile (BM rows x 128 bytes) is assembled in the idle row buffer
+            // and leaves as 16-byte row chunks; chunk c of row r sits at chunk
+            // c ^ ((r / 4) % 8), so the four row groups of one byte write fall
+            // into distinct banks
+            uint8_t* h_tile = reinterpret_cast<uint8_t*>(((nk - 1) & 1) ? sa0 : sa1);
             constexpr int FO = FN / 2;
             float hv[FM][FO][4];
             float rmax[FM][4];
@@ -308,26 +326,38 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                     if ((lane & 15) == 0) s_amax[wn * BM + (wm + WMW * i) * 16 + (lane >> 4) * 4 + e] = m;
                 }
             __syncthreads();
-            uint8_t* Out = static_cast<uint8_t*>(p.out);
+            static_assert(FO == 2 && WN / 2 == 32, "two 16-column chunks per wave and fragment row");
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int mrow = (wm + WMW * i) * 16;
                 if (mrow >= nvalid) continue;
+                const int key = ((mrow >> 2) + (lane >> 4)) & 7;         // (r / 4) % 8 of this lane's rows
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = mrow + (lane >> 4) * 4 + e;
-                    if (r >= nvalid) continue;
                     float amax = 0.f;
 #pragma unroll
                     for (int w = 0; w < WNW; ++w) amax = fmaxf(amax, s_amax[w * BM + r]);
                     const float s = pow2_block_scale(amax);
-                    const float rs = 1.0f / s;       // exact: s is a power of two
-#pragma unroll
-                    for (int f = 0; f < FO; ++f) {
-                        const int col = fcol(f) + (lane & 15);
-                        if (col < N) Out[(size_t)(row0 + r) * N + col] = (uint8_t)f32_to_e4m3_sat(hv[i][f][e] * rs);
-                    }
-                    if (wn == 0 && (lane & 15) == 0) p.out_scales[(size_t)(row0 + r) * nbN + tc.nt] = s;
+                    const float rs = pow2_recip(s);
+                    // |h| <= amax <= 448 s: the hardware conversion needs no saturation
+                    const uint32_t two = e4m3_pair(hv[i][0][e] * rs, hv[i][1][e] * rs);
+                    uint8_t* row = h_tile + r * ROWB + (lane & 15);
+                    row[((2 * wn) ^ key) * 16] = (uint8_t)two;
+                    row[((2 * wn + 1) ^ key) * 16] = (uint8_t)(two >> 8);
+                    if (wn == 0 && (lane & 15) == 0 && r < nvalid)
+                        p.out_scales[(size_t)(row0 + r) * nbN + tc.nt] = s;
+                }
+            }
+            __syncthreads();
+            // rows [0, nvalid) x the valid 16-byte chunks of the tile's columns
+            uint8_t* Out = static_cast<uint8_t*>(p.out);
+            const int nchunk = min(8, (N - col0) / 16);
+            for (int t = tid; t < nvalid * 8; t += NT) {
+                const int r = t >> 3, c = t & 7;
+                if (c < nchunk) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(h_tile + r * ROWB + ((c ^ ((r >> 2) & 7)) * 16));
+                    *reinterpret_cast<uint4*>(Out + (size_t)(row0 + r) * N + col0 + c * 16) = v;
                 }
             }
         } else {

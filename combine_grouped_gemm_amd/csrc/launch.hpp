@@ -59,6 +59,7 @@ struct FfnArgs {
     void* out;                // (cap, N)
     float* out_scales;        // fp8 h only: (cap, ceil(N/128))
     int rows_hint;            // cap / E_loc, picks the tile shape
+    bool w_scales_pow2;       // fp8: every weight scale is a power of two
 };
 
 hipError_t launch_ffn_f32(const FfnArgs& a, bool gated, hipStream_t stream);   // ffn_f32.hip

@@ -114,11 +114,13 @@ class MoELayer:
     def gate_up(self, w, stream=None):
         moe_ffn_gate_up(self.xd, self.xd_scales, self.rows, w["gate"], w["up"],
                         w.get("gate_scale"), w.get("up_scale"), self.h, self.h_scales,
-                        expected_rows=self.expected_rows, stream=stream, cap_per_expert=self.cap_e)
+                        expected_rows=self.expected_rows, stream=stream, cap_per_expert=self.cap_e,
+                        w_scales_pow2=bool(w.get("scales_pow2", False)))
 
     def down(self, w, stream=None):
         moe_ffn_down(self.h, self.h_scales, self.rows, w["down"], w.get("down_scale"), self.y,
-                     expected_rows=self.expected_rows, stream=stream, cap_per_expert=self.cap_e)
+                     expected_rows=self.expected_rows, stream=stream, cap_per_expert=self.cap_e,
+                     w_scales_pow2=bool(w.get("scales_pow2", False)))
 
     def combine(self, stream=None):
         moe_combine(self.y, self.row_of, self.topk_w, self.out, stream=stream)

@@ -56,7 +56,11 @@ typedef enum {
 typedef enum {
     MOE_F32 = 0,
     MOE_BF16 = 1,
-    MOE_FP8_E4M3 = 2           /* OCP e4m3fn (finite max 448), with fp32 1x128 block scales */
+    MOE_FP8_E4M3 = 2,          /* OCP e4m3fn (finite max 448), with fp32 1x128 block scales */
+    MOE_FP8_E4M3_PO2 = 3       /* weights only: e4m3fn whose fp32 block scales are all powers
+                                  of two 2^e, e in [-127, 127] (the E8M0 scale convention of
+                                  the microscaling formats); the matrix cores apply such
+                                  scales, and only a scale's exponent field is read */
 } moe_dtype_t;
 
 /* Largest number of simulated source segments moe_dispatch accepts. */
@@ -231,7 +235,11 @@ moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int
  * offsets[E_local] of h and y are not written.
  *
  * Supported (act_dt, w_dt, y_dt): (F32, F32, F32), (BF16, BF16, BF16),
- * (FP8_E4M3, FP8_E4M3, BF16).
+ * (FP8_E4M3, FP8_E4M3, BF16), (FP8_E4M3, FP8_E4M3_PO2, BF16).  The
+ * activation block scales of the fp8 path (xd_scales from moe_dispatch,
+ * h_scales) are always powers of two; FP8_E4M3_PO2 declares that the
+ * weight scales are too, which lets the row-rich kernels apply every scale
+ * in the matrix cores (same results up to fp32 rounding order).
  *
  * moe_ffn_gate_up computes h; moe_ffn_down computes y from h;
  * moe_grouped_ffn runs both with h (and h_scales) carved from `ws`, which

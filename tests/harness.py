@@ -63,10 +63,7 @@ class Case:
         self.x_dev = [s.to(device) for s in self.x_cpu]
         self.logits_dev = self.logits_cpu.to(device)
         self.w = wl.gen_expert_weights(cfg, device=device)
-        self.wdict = {"gate": self.w.gate, "up": self.w.up, "down": self.w.down}
-        if cfg.w_dtype == "fp8":
-            self.wdict.update(gate_scale=self.w.gate_scale, up_scale=self.w.up_scale,
-                              down_scale=self.w.down_scale)
+        self.wdict = self.w.as_dict()
 
     # oracle views --------------------------------------------------------------
     def x_np(self) -> np.ndarray:

@@ -85,6 +85,12 @@ def test_ffn_rejects():
     assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 2, p, p, None, None, 2, p, None, 0, None) == 1
     # fp8 activations need a bf16 y
     assert L.moe_ffn_down(p, p, p, 8, 64, 128, 128, 2, p, p, 2, p, 2, 0, None) == 2
+    # power-of-two-scale fp8 is a weight dtype only: not with bf16 activations, not as activations
+    assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 1, p, p, None, None, 3, p, None, 0, None) == 2
+    assert L.moe_ffn_gate_up(p, p, p, 8, 64, 128, 128, 3, p, p, p, p, 3, p, p, 0, None) == 2
+    assert L.moe_ffn_down(p, p, p, 8, 64, 128, 128, 2, p, None, 3, p, 1, 0, None) == 1   # scales needed
+    assert L.moe_dispatch(ctypes.cast((ctypes.c_void_p * 1)(4096), ctypes.POINTER(ctypes.c_void_p)),
+                          (ctypes.c_int32 * 1)(4), 1, 1, 128, p, 2, p, 3, p, 8, None) == 2
     # workspace too small
     assert L.moe_grouped_ffn(p, None, p, 8, 64, 128, 128, 1, p, p, p, None, None, None, 1, p, 1,
                              p, 16, 0, None) == 1

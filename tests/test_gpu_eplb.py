@@ -52,7 +52,7 @@ def test_layer_on_balanced_placement():
     logical_of_phys = np.argsort(phys)
     local_logical = [int(e) for e in logical_of_phys[cfg.e_begin:cfg.e_end]]
     W = wl.gen_expert_weights(cfg, device="cuda", experts=local_logical)
-    w = {"gate": W.gate, "up": W.up, "down": W.down}
+    w = W.as_dict()
     layer = MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end, cfg.act_dtype,
                      cfg.y_dtype, cfg.out_dtype)
     layer.expert_map = torch.from_numpy(phys.astype(np.int32)).cuda()

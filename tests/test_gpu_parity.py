@@ -28,6 +28,10 @@ SMALL = [
     wl.scaled(C["ep8_share"], "ep_small", seg_rows=(100, 37, 64), E=16, K=3, H=256, I=128,
               e_begin=4, e_end=10),
     wl.scaled(C["gptoss_fp8"], "fp8_small", seg_rows=(300,), E=8, K=2, H=320, I=192),
+    wl.scaled(C["gptoss_fp8"], "fp8_small_f32_wscales", seg_rows=(300,), E=8, K=2, H=320, I=192,
+              w_scales="fp32"),
+    wl.scaled(C["gptoss_fp8"], "fp8_wide_f32_wscales", seg_rows=(600,), E=8, K=2, H=640, I=384,
+              w_scales="fp32"),
     wl.scaled(C["gptoss_fp8"], "fp8_decode_real_dims", seg_rows=(24,), E=16, K=4),
 ]
 
@@ -150,10 +154,39 @@ def test_fp8_grouped_call_matches_stage_calls():
     w = case.wdict
     y2 = moe_grouped_ffn(layer.xd, layer.xd_scales, layer.offsets, w["gate"], w["up"], w["down"],
                          w["gate_scale"], w["up_scale"], w["down_scale"],
-                         expected_rows=layer.expected_rows)
+                         expected_rows=layer.expected_rows, w_scales_pow2=w["scales_pow2"])
     torch.cuda.synchronize()
     R = int(layer.offsets[-1])
     assert torch.equal(y2[:R], layer.y[:R])
+
+
+def test_fp8_pow2_weight_path_matches_generic_path():
+    """Power-of-two weight scales declared (MOE_FP8_E4M3_PO2: every scale
+    applied by the matrix cores) or not (weight scale folded in fp32 per
+    block product): the same numbers up to fp32 rounding order, so y agrees
+    far inside the fp8 tolerance and h codes differ only where a value sits
+    on a rounding boundary."""
+    from combine_grouped_gemm_amd import moe_ffn_down, moe_ffn_gate_up
+    cfg = wl.scaled(C["gptoss_fp8"], "fp8_po2_vs_generic", seg_rows=(600,), E=8, K=2, H=640, I=384)
+    case = Case(cfg)
+    assert case.w.scales_pow2
+    layer = run_gpu(case)
+    w = case.wdict
+    kw = dict(expected_rows=layer.expected_rows)
+    res = {}
+    for po2 in (True, False):
+        h, hs = moe_ffn_gate_up(layer.xd, layer.xd_scales, layer.offsets, w["gate"], w["up"],
+                                w["gate_scale"], w["up_scale"], w_scales_pow2=po2, **kw)
+        y = moe_ffn_down(h, hs, layer.offsets, w["down"], w["down_scale"], w_scales_pow2=po2, **kw)
+        torch.cuda.synchronize()
+        res[po2] = (h, hs, y)
+    R = int(layer.offsets[-1])
+    assert torch.equal(res[True][2][:R], layer.y[:R])          # the layer took the PO2 path
+    codes_t = res[True][0][:R].view(torch.uint8)
+    codes_f = res[False][0][:R].view(torch.uint8)
+    assert (codes_t != codes_f).float().mean().item() < 1e-2
+    yt, yf = res[True][2][:R].double(), res[False][2][:R].double()
+    assert ((yt - yf).norm() / yf.norm()).item() < 1e-2
 
 
 def test_deterministic_and_stage_split_matches_grouped_call():

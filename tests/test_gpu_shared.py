@@ -31,9 +31,7 @@ def test_layer_with_shared_experts(cfg, ns):
     x_cpu = wl.gen_x(cfg)
     logits_cpu = wl.gen_logits(cfg, x_cpu)
     W = wl.gen_expert_weights(cfg, device="cuda", experts=list(range(cfg.E + ns)))
-    w = {"gate": W.gate, "up": W.up, "down": W.down}
-    if cfg.w_dtype == "fp8":
-        w.update(gate_scale=W.gate_scale, up_scale=W.up_scale, down_scale=W.down_scale)
+    w = W.as_dict()
     layer = MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, 0, cfg.E, cfg.act_dtype, cfg.y_dtype,
                      cfg.out_dtype, n_shared=ns)
     layer.forward([s.cuda() for s in x_cpu], logits_cpu.cuda(), w)

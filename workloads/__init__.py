@@ -52,6 +52,7 @@ class MoEConfig:
     seed: int
     zipf_bias: bool = False
     description: str = ""
+    w_scales: str = "fp32"   # fp8 weight block scales: 'fp32' (any positive value) | 'pow2'
 
     @property
     def T(self) -> int:
@@ -89,12 +90,13 @@ CONFIGS = {
     "gptoss_fp8": MoEConfig("gptoss_fp8", (4096,), 128, 4, 2880, 2880, 0, 128,
                             "bf16", "fp8", "fp8", "bf16", "bf16", seed=5,
                             description="GPT-OSS-120B-shaped layer, fp8 e4m3 weights and "
-                                        "activations with 1x128 fp32 block scales"),
+                                        "activations with 1x128 fp32 block scales (powers of two)",
+                            w_scales="pow2"),
 }
 
 
 def scaled(cfg: MoEConfig, name: str, *, seg_rows=None, E=None, K=None, H=None, I=None,
-           e_begin=None, e_end=None, seed=None) -> MoEConfig:
+           e_begin=None, e_end=None, seed=None, w_scales=None) -> MoEConfig:
     """A smaller (or otherwise changed) copy of a workload, for parity tests."""
     E = cfg.E if E is None else E
     kw = dict(name=name,
@@ -104,6 +106,7 @@ def scaled(cfg: MoEConfig, name: str, *, seg_rows=None, E=None, K=None, H=None, 
               e_begin=0 if e_begin is None else e_begin,
               e_end=E if e_end is None else e_end,
               seed=cfg.seed if seed is None else seed,
+              w_scales=cfg.w_scales if w_scales is None else w_scales,
               zipf_bias=False)           # the calibrated bias belongs to the named workload only
     return replace(cfg, **kw)
 
@@ -200,6 +203,15 @@ class ExpertWeights:
     up_scale: torch.Tensor = None
     down_scale: torch.Tensor = None
     dtype: str = "bf16"
+    scales_pow2: bool = False      # fp8: every block scale is a power of two
+
+    def as_dict(self) -> dict:
+        """The tensors as the layer takes them (no copies)."""
+        d = {"gate": self.gate, "up": self.up, "down": self.down}
+        if self.dtype == "fp8":
+            d.update(gate_scale=self.gate_scale, up_scale=self.up_scale,
+                     down_scale=self.down_scale, scales_pow2=self.scales_pow2)
+        return d
 
     def expert(self, e: int, device="cpu") -> dict:
         """Copies of local expert e's tensors on ``device``."""
@@ -232,7 +244,10 @@ def gen_expert_weights(cfg: MoEConfig, device="cpu", experts=None) -> ExpertWeig
     fp8 weights are drawn as codes and scales directly: codes ~ e4m3 cast
     of N(0, 1) * 64 clamped to +-448, and per-block scales
     s = (1 / (64 * sqrt(fan_in))) * exp(0.1 * N(0, 1)), so code * scale has
-    roughly the N(0, 1/fan_in) spread of the other workloads.
+    roughly the N(0, 1/fan_in) spread of the other workloads.  With
+    cfg.w_scales == 'pow2' the scales are powers of two instead,
+    s = 2^(round(log2(1 / (64 * sqrt(fan_in)))) + n) with n = N(0, 1)
+    rounded and clamped to [-2, 2].
     """
     experts = list(range(cfg.e_begin, cfg.e_end)) if experts is None else [int(e) for e in experts]
     E_loc, H, I = len(experts), cfg.H, cfg.I
@@ -258,7 +273,12 @@ def gen_expert_weights(cfg: MoEConfig, device="cpu", experts=None) -> ExpertWeig
                 codes[w][j].copy_(c.to(torch.float8_e4m3fn))
                 nb = scales[w].shape[2]
                 z = torch.randn((s[0], nb), generator=g, device=device)
-                scales[w][j].copy_(torch.exp(0.1 * z) / (64.0 * math.sqrt(s[1])))
+                if cfg.w_scales == "pow2":
+                    e0 = round(math.log2(1.0 / (64.0 * math.sqrt(s[1]))))
+                    n = torch.round(z).clamp_(-2.0, 2.0).to(torch.int32)
+                    scales[w][j].copy_(((n + (e0 + 127)) << 23).view(torch.float32))   # exact 2^(e0+n)
+                else:
+                    scales[w][j].copy_(torch.exp(0.1 * z) / (64.0 * math.sqrt(s[1])))
         return ExpertWeights(codes[0], codes[1], codes[2], scales[0], scales[1], scales[2],
-                             dtype="fp8")
+                             dtype="fp8", scales_pow2=cfg.w_scales == "pow2")
     raise ValueError(cfg.w_dtype)
