@@ -94,6 +94,19 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// Maximum over the 16 lanes of a DPP row (lanes 16k .. 16k + 15), returned in
+// every lane of the row, by cross-lane moves inside the VALU: quad permutes
+// [1,0,3,2] and [2,3,0,1] (partners lane ^ 1 and lane ^ 2), then the half-row
+// mirror (lane i <-> 7 - i: joins the two quads of each half) and the row
+// mirror (lane i <-> 15 - i: joins the two halves).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // wave helpers
 // ---------------------------------------------------------------------------

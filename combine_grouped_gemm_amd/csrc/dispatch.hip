@@ -11,8 +11,8 @@
 // destination row of the token, so a decode-sized batch still spreads over
 // the whole chip.  Plain stores: the non-temporal hint made this kernel
 // slower in the layer's sequence.  For fp8 storage the token is quantised once per
-// 128-element block (16 lanes of one wave cover a block; amax by xor shuffles
-// inside the 16-lane group) and every copy receives the same codes and scale.
+// 128-element block (the 16 lanes of a DPP row cover a block; amax by
+// cross-lane moves inside the row) and every copy receives the same codes and scale.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -44,8 +44,8 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_copy_kernel(
 }
 
 // bf16 -> fp8 e4m3 with one fp32 scale per 128 elements.  A block's slice
-// starts at a multiple of 256 vectors, so the 16 vectors of a scale block are
-// 16 consecutive lanes of one wave.
+// starts at a multiple of 16 vectors, so the 16 vectors of a scale block are
+// the 16 lanes of one DPP row of a wave.
 __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
     SegTable seg, int H, const int32_t* __restrict__ row_of, int K, int cap,
     uint8_t* __restrict__ xd, float* __restrict__ xd_scales) {
@@ -61,8 +61,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+    amax = row16_max(amax);
     if (!ok) return;
     const float s = pow2_block_scale(amax);
     const float rs = 1.0f / s;               // exact: s is a power of two

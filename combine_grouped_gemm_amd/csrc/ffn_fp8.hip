@@ -16,8 +16,8 @@
 // on both operands.
 //
 // gate/up writes h as fp8: each tile covers exactly one 128-column block of
-// h per row, so the block amax is reduced inside the tile (16 lanes by xor
-// shuffles, then the waves of a row through LDS), s is the smallest power of
+// h per row, so the block amax is reduced inside the tile (the 16 lanes of a
+// DPP row, then the waves of a row through LDS), s is the smallest power of
 // two with amax <= 448 s, and the codes are written with the scale.
 #include "gemm_wide_fp8.hpp"
 #include "grouped_tiles.hpp"
@@ -239,9 +239,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float m = rmax[i][e];
-#pragma unroll
-                    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+                    const float m = row16_max(rmax[i][e]);
                     if ((lane & 15) == 0) s_amax[wn][(wm + WMW * i) * 16 + (lane >> 4) * 4 + e] = m;
                 }
             __syncthreads();

@@ -110,50 +110,48 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     // block start at multiples of 8, so (row & 7) = lane / 8
     const int lchunk = wide::swz(lane / 8, lane % 8);
 
-    for (int tau = v; tau < total; tau += G) {
-        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p);
+    // ---- load state: the tile whose operands the direct loads fetch.  The
+    // next tile's scales and first k-step are issued as soon as every wave has
+    // finished the current tile's k-loop, so their latency hides behind the
+    // current tile's epilogue (which then works in the second stage's buffers).
+    const bool w_lines = Kdim % 128 == 0;
+    const char* abase = nullptr;
+    const char* gbase = nullptr;
+    const char* ubase = nullptr;
+    uint32_t off[LPS];
+
+    // decode tile t, copy its scales to LDS and set the load state.  Scales go
+    // row-major with a fixed row stride of SK = kMaxKBlocks floats ([tile
+    // row][k-block]; odd, so the 16 rows one MFMA operand touches fall into
+    // distinct banks).  Global scales are [row][k-block] with nk per row, so
+    // 4-byte direct loads over the flat index e = row * SK + k read one
+    // contiguous run per tile (a few cache lines per load); lanes with k >= nk
+    // or past the valid rows / columns re-read element 0, whose value no
+    // output uses.  Operand offsets are 32-bit, relative to the tile's first
+    // row or to the expert's weight matrices; wave w loads the 1 KiB blocks
+    // w, w + NW, ... of a stage (8 rows each; row blocks first, then weight
+    // blocks); rows / columns past the valid ones re-read row 0.
+    auto stage_tile = [&](int t) -> TileCoord {
+        const TileCoord tc = decode_tile<BM>(t, n_tiles_n, s_pre, p);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
-        const uint8_t* wg = W0 + (size_t)j * N * Kdim;
-        const uint8_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
         const float* wgs = p.w0_scales + (size_t)j * N * nk;
         const float* wus = GATED ? p.w1_scales + (size_t)j * N * nk : nullptr;
-
-        // the previous tile's reads of the stages and of the scales are complete
-        wide::wait_lgkm0();
-        wide::block_barrier();
-
-        // ---- this tile's scales -> LDS, row-major with a fixed row stride of
-        // SK = kMaxKBlocks floats ([tile row][k-block]; odd, so the 16 rows one
-        // MFMA operand touches fall into distinct banks).  Global scales are
-        // [row][k-block] with nk per row, so 4-byte direct loads over the flat
-        // index e = row * SK + k read one contiguous run per tile (a few cache
-        // lines per load); lanes with k >= nk or past the valid rows / columns
-        // re-read element 0, whose value no output uses.
-        {
-            const float* asrc = p.a_scales + (size_t)row0 * nk;
-            for (int q = wave; q < BM * SK / kWave; q += NW) {
-                const int e = q * kWave + lane, r = e / SK, k = e - r * SK;
-                lds_dma4(asrc + (r < nvalid && k < nk ? r * nk + k : 0), s_as + q * kWave);
-            }
-            for (int q = wave; q < BN * SK / kWave; q += NW) {
-                const int e = q * kWave + lane, c = e / SK, k = e - c * SK;      // tile weight row c
-                const bool up = GATED && c >= BN / 2;
-                const int col = col0 + (up ? c - BN / 2 : c);
-                const float* bsrc = up ? wus : wgs;
-                lds_dma4(bsrc + (col < N && k < nk ? (size_t)col * nk + k : 0), s_bs + q * kWave);
-            }
+        const float* asrc = p.a_scales + (size_t)row0 * nk;
+        for (int q = wave; q < BM * SK / kWave; q += NW) {
+            const int e = q * kWave + lane, r = e / SK, k = e - r * SK;
+            lds_dma4(asrc + (r < nvalid && k < nk ? r * nk + k : 0), s_as + q * kWave);
         }
-        const bool w_lines = Kdim % 128 == 0;
-        // per-lane source offsets (32-bit, relative to the tile's first row or to
-        // the expert's weight matrices).  Wave w loads the 1 KiB blocks w, w + NW, ...
-        // of a stage (8 rows each; row blocks first, then weight blocks); rows /
-        // columns past the valid ones re-read row 0.  Every wave issues LPS
-        // loads per stage.
-        const char* abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
-        const char* gbase = reinterpret_cast<const char*>(wg);
-        const char* ubase = reinterpret_cast<const char*>(wu);
-        uint32_t off[LPS];
+        for (int q = wave; q < BN * SK / kWave; q += NW) {
+            const int e = q * kWave + lane, c = e / SK, k = e - c * SK;      // tile weight row c
+            const bool up = GATED && c >= BN / 2;
+            const int col = col0 + (up ? c - BN / 2 : c);
+            const float* bsrc = up ? wus : wgs;
+            lds_dma4(bsrc + (col < N && k < nk ? (size_t)col * nk + k : 0), s_bs + q * kWave);
+        }
+        abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
+        gbase = reinterpret_cast<const char*>(W0 + (size_t)j * N * Kdim);
+        ubase = GATED ? reinterpret_cast<const char*>(W1 + (size_t)j * N * Kdim) : nullptr;
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
             const int q = i * NW + wave;                 // wave-uniform
@@ -168,32 +166,43 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 off[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)Kdim + c16;
             }
         }
-        // Weight rows are streamed with the non-temporal hint only when they start
-        // on 128-byte lines: otherwise a k-step's 128 bytes straddle two lines and
-        // the next k-step re-reads the second one, which must still be in L2.
-        auto issue_p = [&](auto I, int kstep, auto WPOL) {
-            const uint32_t kb = (uint32_t)kstep * ROWB;
-            // in a 64-byte tail block, chunks 4..7 come from the zero block
-            const bool zl = k_tail && kstep == nk - 1 && lchunk >= 4;
+        return tc;
+    };
+    // Weight rows are streamed with the non-temporal hint only when they start
+    // on 128-byte lines: otherwise a k-step's 128 bytes straddle two lines and
+    // the next k-step re-reads the second one, which must still be in L2.
+    auto issue_p = [&](auto I, int kstep, auto WPOL) {
+        const uint32_t kb = (uint32_t)kstep * ROWB;
+        // in a 64-byte tail block, chunks 4..7 come from the zero block
+        const bool zl = k_tail && kstep == nk - 1 && lchunk >= 4;
 #pragma unroll
-            for (int i = 0; i < LPS; ++i) {
-                const int q = i * NW + wave;
-                if (q >= BLOCKS) break;                  // wave-uniform
-                const bool is_a = q < A_BLOCKS;
-                const bool up = GATED && !is_a && (q - A_BLOCKS) * 8 >= BN / 2;
-                const char* b = is_a ? abase : (up ? ubase : gbase);
-                char* dst = is_a ? a_base(I) + q * 1024 : b_base(I) + (q - A_BLOCKS) * 1024;
-                const char* src = zl ? reinterpret_cast<const char*>(kZeroChunk) : b + off[i] + kb;
-                if (is_a)
-                    wide::lds_dma16<0>(src, dst);
-                else
-                    wide::lds_dma16<decltype(WPOL)::value>(src, dst);
-            }
-        };
-        auto issue = [&](auto I, int kstep) {
-            if (w_lines) issue_p(I, kstep, ic<wide::kNonTemporal>{});
-            else issue_p(I, kstep, ic<0>{});
-        };
+        for (int i = 0; i < LPS; ++i) {
+            const int q = i * NW + wave;
+            if (q >= BLOCKS) break;                      // wave-uniform
+            const bool is_a = q < A_BLOCKS;
+            const bool up = GATED && !is_a && (q - A_BLOCKS) * 8 >= BN / 2;
+            const char* b = is_a ? abase : (up ? ubase : gbase);
+            char* dst = is_a ? a_base(I) + q * 1024 : b_base(I) + (q - A_BLOCKS) * 1024;
+            const char* src = zl ? reinterpret_cast<const char*>(kZeroChunk) : b + off[i] + kb;
+            if (is_a)
+                wide::lds_dma16<0>(src, dst);
+            else
+                wide::lds_dma16<decltype(WPOL)::value>(src, dst);
+        }
+    };
+    auto issue = [&](auto I, int kstep) {
+        if (w_lines) issue_p(I, kstep, ic<wide::kNonTemporal>{});
+        else issue_p(I, kstep, ic<0>{});
+    };
+
+    TileCoord cur{};
+    if (v < total) {
+        cur = stage_tile(v);
+        issue(ic<0>{}, 0);
+    }
+    for (int tau = v; tau < total; tau += G) {
+        const int row0 = cur.row0, nvalid = cur.nvalid, nt = cur.nt;
+        const int col0 = nt * BNO;
 
         floatx4 acc[FM][FN];
 #pragma unroll
@@ -270,7 +279,6 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             }
         };
 
-        issue(ic<0>{}, 0);
         // step k: wait for stage k (nothing else is in flight), then load k+1
         // into the other buffer while computing k
         auto step = [&](auto I, int k) {
@@ -286,18 +294,30 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             if (k + 1 < nk) step(ic<1>{}, k + 1);
         }
 
-        // ---- epilogue
+        // every wave is done with both stages and the scale tables: start the
+        // next tile's loads into stage 0 and the scale tables
+        wide::wait_lgkm0();
+        wide::block_barrier();
+        if (tau + G < total) {
+            cur = stage_tile(tau + G);
+            issue(ic<0>{}, 0);
+        }
+
+        // ---- epilogue (LDS: only the second stage's buffers; the barriers wait
+        // for LDS traffic, not for the next tile's loads in flight)
         if constexpr (GATED) {
             // h = silu(g) * u; the tile's 128 columns are one scale block of h:
-            // row amax over 16 lanes (shuffles) and the 4 column waves, through
-            // the row stage the last k-step did not read (every wave has passed
-            // the barrier after its last read, and no load is in flight)
-            float* s_amax = reinterpret_cast<float*>(((nk - 1) & 1) ? sb0 : sb1);
-            // the h tile (BM rows x 128 bytes) is assembled in the idle row buffer
+            // row amax over 16 lanes (DPP row) and the 4 column waves
+            float* s_amax = reinterpret_cast<float*>(sb1);
+            // the h tile (BM rows x 128 bytes) is assembled in the row buffer
             // and leaves as 16-byte row chunks; chunk c of row r sits at chunk
             // c ^ ((r / 4) % 8), so the four row groups of one byte write fall
             // into distinct banks
-            uint8_t* h_tile = reinterpret_cast<uint8_t*>(((nk - 1) & 1) ? sa0 : sa1);
+            uint8_t* h_tile = reinterpret_cast<uint8_t*>(sa1);
+            // row scales of h, stored with the tile (no global store inside the
+            // loop above: a wait for one would also wait for the loads in flight)
+            float* s_hscale = s_amax + WNW * BM;
+            static_assert((WNW + 1) * BM * 4 <= BN * ROWB, "amax partials and row scales fit the weight buffer");
             constexpr int FO = FN / 2;
             float hv[FM][FO][4];
             float rmax[FM][4];
@@ -320,12 +340,11 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float m = rmax[i][e];
-#pragma unroll
-                    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+                    const float m = row16_max(rmax[i][e]);
                     if ((lane & 15) == 0) s_amax[wn * BM + (wm + WMW * i) * 16 + (lane >> 4) * 4 + e] = m;
                 }
-            __syncthreads();
+            wide::wait_lgkm0();
+            wide::block_barrier();
             static_assert(FO == 2 && WN / 2 == 32, "two 16-column chunks per wave and fragment row");
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -345,11 +364,11 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                     uint8_t* row = h_tile + r * ROWB + (lane & 15);
                     row[((2 * wn) ^ key) * 16] = (uint8_t)two;
                     row[((2 * wn + 1) ^ key) * 16] = (uint8_t)(two >> 8);
-                    if (wn == 0 && (lane & 15) == 0 && r < nvalid)
-                        p.out_scales[(size_t)(row0 + r) * nbN + tc.nt] = s;
+                    if (wn == 0 && (lane & 15) == 0) s_hscale[r] = s;
                 }
             }
-            __syncthreads();
+            wide::wait_lgkm0();
+            wide::block_barrier();
             // rows [0, nvalid) x the valid 16-byte chunks of the tile's columns
             uint8_t* Out = static_cast<uint8_t*>(p.out);
             const int nchunk = min(8, (N - col0) / 16);
@@ -360,6 +379,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                     *reinterpret_cast<uint4*>(Out + (size_t)(row0 + r) * N + col0 + c * 16) = v;
                 }
             }
+            for (int r = tid; r < nvalid; r += NT) p.out_scales[(size_t)(row0 + r) * nbN + nt] = s_hscale[r];
         } else {
             uint16_t* Out = static_cast<uint16_t*>(p.out);
 #pragma unroll
