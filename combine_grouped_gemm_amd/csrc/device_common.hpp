@@ -31,16 +31,19 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Round to nearest even; NaN stays NaN, overflow becomes inf.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// f32 -> bf16, round to nearest even, by gfx950's packed conversion
+// (v_cvt_pk_bf16_f32; bit-identical to the integer RNE
+// (u + 0x7fff + ((u >> 16) & 1)) >> 16 on every finite input, checked on the
+// GPU across all exponents, denormals, ties and the overflow boundary).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    const bf16x2_t b = __builtin_convertvector(float2_t{lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 // ---------------------------------------------------------------------------
 // OCP fp8 e4m3fn: encode with round-to-nearest-even after saturating the

@@ -100,6 +100,12 @@ __device__ __forceinline__ TileCoord decode_tile(int tau, int n_tiles_n, const i
     const int n = r1 - r0;
     t.row0 = r0 + (int)(((long long)n * mt) / mt_j);
     t.nvalid = r0 + (int)(((long long)n * (mt + 1)) / mt_j) - t.row0;
+    // every lane computed the same values: keep them in scalar registers, so
+    // tile base addresses are scalar and stores can use 32-bit lane offsets
+    t.j = __builtin_amdgcn_readfirstlane(t.j);
+    t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+    t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+    t.nvalid = __builtin_amdgcn_readfirstlane(t.nvalid);
     return t;
 }
 
