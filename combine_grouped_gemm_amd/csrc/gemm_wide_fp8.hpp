@@ -317,7 +317,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             // row scales of h, stored with the tile (no global store inside the
             // loop above: a wait for one would also wait for the loads in flight)
             float* s_hscale = s_amax + WNW * BM;
-            static_assert((WNW + 1) * BM * 4 <= BN * ROWB, "amax partials and row scales fit the weight buffer");
+            static_assert((WNW + 2) * BM * 4 <= BN * ROWB, "amax partials, row scales and reciprocals fit the weight buffer");
             constexpr int FO = FN / 2;
             float hv[FM][FO][4];
             float rmax[FM][4];
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 for (int f = 0; f < FO; ++f)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const bool ok = fcol(f) + (lane & 15) < N;
+                        const bool ok = fcol(f) < N;        // wave-uniform: N is a multiple of 16
                         const float h = ok ? silu(acc[i][f][e]) * acc[i][f + FO][e] : 0.f;
                         hv[i][f][e] = h;
                         rmax[i][e] = fmaxf(rmax[i][e], fabsf(h));
@@ -345,6 +345,18 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 }
             wide::wait_lgkm0();
             wide::block_barrier();
+            // one thread per row: the row's scale and its reciprocal
+            float* s_hrs = s_hscale + BM;
+            for (int r = tid; r < BM; r += NT) {
+                float amax = 0.f;
+#pragma unroll
+                for (int w = 0; w < WNW; ++w) amax = fmaxf(amax, s_amax[w * BM + r]);
+                const float s = pow2_block_scale(amax);
+                s_hscale[r] = s;
+                s_hrs[r] = pow2_recip(s);
+            }
+            wide::wait_lgkm0();
+            wide::block_barrier();
             static_assert(FO == 2 && WN / 2 == 32, "two 16-column chunks per wave and fragment row");
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -354,17 +366,12 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = mrow + (lane >> 4) * 4 + e;
-                    float amax = 0.f;
-#pragma unroll
-                    for (int w = 0; w < WNW; ++w) amax = fmaxf(amax, s_amax[w * BM + r]);
-                    const float s = pow2_block_scale(amax);
-                    const float rs = pow2_recip(s);
+                    const float rs = s_hrs[r];
                     // |h| <= amax <= 448 s: the hardware conversion needs no saturation
                     const uint32_t two = e4m3_pair(hv[i][0][e] * rs, hv[i][1][e] * rs);
                     uint8_t* row = h_tile + r * ROWB + (lane & 15);
                     row[((2 * wn) ^ key) * 16] = (uint8_t)two;
                     row[((2 * wn + 1) ^ key) * 16] = (uint8_t)(two >> 8);
-                    if (wn == 0 && (lane & 15) == 0) s_hscale[r] = s;
                 }
             }
             wide::wait_lgkm0();

@@ -33,6 +33,10 @@ SMALL = [
     wl.scaled(C["gptoss_fp8"], "fp8_wide_f32_wscales", seg_rows=(600,), E=8, K=2, H=640, I=384,
               w_scales="fp32"),
     wl.scaled(C["gptoss_fp8"], "fp8_decode_real_dims", seg_rows=(24,), E=16, K=4),
+    # H = I = 2880: 23 scale blocks per row (whole-row scale runs) and a 64-wide K tail,
+    # 48 rows per expert (the wide fp8 tiles), both weight-scale conventions
+    wl.scaled(C["gptoss_fp8"], "fp8_wide_real_dims", seg_rows=(192,), E=8, K=2),
+    wl.scaled(C["gptoss_fp8"], "fp8_wide_real_dims_f32_wscales", seg_rows=(200,), E=8, K=2, w_scales="fp32"),
 ]
 
 
