@@ -37,6 +37,9 @@ SMALL = [
     # 48 rows per expert (the wide fp8 tiles), both weight-scale conventions
     wl.scaled(C["gptoss_fp8"], "fp8_wide_real_dims", seg_rows=(192,), E=8, K=2),
     wl.scaled(C["gptoss_fp8"], "fp8_wide_real_dims_f32_wscales", seg_rows=(200,), E=8, K=2, w_scales="fp32"),
+    # fp8 at DeepSeek dimensions: 56 scale blocks per row (past the wide tiles' scale table),
+    # ~32 rows per expert through the 128-row fp8 tiles
+    wl.scaled(C["gptoss_fp8"], "fp8_dsv3_dims", seg_rows=(64,), E=16, K=8, H=7168, I=2048),
 ]
 
 
