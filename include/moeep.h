@@ -208,8 +208,10 @@ moe_status_t moe_layout_masked(const int32_t* topk_ids, int B, int K, int E, int
  *   xd_scales (cap_rows, ceil(H/128)) fp32 out, fp8 only (else may be NULL).
  * Supported (x_dt -> xd_dt): F32 -> F32 and BF16 -> BF16 (bit-exact
  * copies); BF16 -> FP8_E4M3 (each token quantised once: per 128-element
- * block s = amax/448 (1 if amax = 0), code = RNE(v/s) saturated to +-448,
- * with fp32 arithmetic; all K copies carry identical codes and scales).
+ * block s = the smallest power of two 2^e with amax <= 448 * 2^e, e >= -127
+ * (1 if amax = 0; the E8M0 scale convention), code = RNE(v/s) saturated to
+ * +-448, with fp32 arithmetic; all K copies carry identical codes and
+ * scales).
  */
 moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int n_seg,
                           moe_dtype_t x_dt, int H, const int32_t* row_of, int K,
