@@ -82,10 +82,11 @@ def _forced_case(cfg, logits):
     return case
 
 
-@pytest.mark.parametrize("act,T", [("bf16", 300), ("bf16", 600), ("fp8", 300)])
+@pytest.mark.parametrize("act,T", [("bf16", 300), ("bf16", 600), ("fp8", 300), ("fp8", 600)])
 def test_all_tokens_one_expert_rest_empty(act, T):
     """All rows on one expert (several m-tiles of the 128-row and of the
-    256-row kernels, split evenly), seven experts empty."""
+    256-row kernels, split evenly; for fp8 at T = 600 the 192-row wide
+    tiles), seven experts empty."""
     base = C["dsv3_prefill"] if act == "bf16" else C["gptoss_fp8"]
     cfg = wl.scaled(base, f"one_expert_{act}_{T}", seg_rows=(T,), E=8, K=1, H=256, I=192)
     lg = np.random.default_rng(0).normal(size=(T, 8)).astype(np.float32)
