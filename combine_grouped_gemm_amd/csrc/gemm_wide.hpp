@@ -165,10 +165,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
                                  : b_base(I) + ((i - A_ITERS) * NW + wave) * 1024;
                 // weight tiles are read by one or two m-tiles of an expert, all
                 // close together in tile order; the row block is re-read by
-                // every n-tile, so only the weights stream
-                if (is_a)
-                    lds_dma16<0>(b + off[i] + (size_t)kstep * BK * 2, dst);
-                else
+                // every n-tile, so only the weights stream.  Row blocks wholly
+                // past the valid rows are not loaded (wave-uniform): their
+                // stale LDS rows feed only outputs that are never stored.
+                if (is_a) {
+                    if ((i * NW + wave) * 8 < nvalid) lds_dma16<0>(b + off[i] + (size_t)kstep * BK * 2, dst);
+                } else
                     lds_dma16<kNonTemporal>(b + off[i] + (size_t)kstep * BK * 2, dst);
             }
         };
