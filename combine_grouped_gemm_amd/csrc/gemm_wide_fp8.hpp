@@ -3,8 +3,10 @@
 // used by ffn_fp8.hip.
 //
 // Same ragged persistent tile walk and direct global-to-LDS two-stage ring as
-// the wide bf16 kernel (every step waits for all loads in flight); one k-step is one 128-byte scale block, so the LDS
-// row geometry (8 swizzled 16-byte chunks per row) is identical.  A tile is
+// the wide bf16 kernel (every step waits for all loads in flight); one k-step
+// is one 128-byte scale block, so the LDS row geometry (8 swizzled 16-byte
+// chunks per row) is identical.  The next tile's scales and first k-step are
+// loaded while the current tile's epilogue runs.  A tile is
 // up to 192 rows of one expert by 256 weight rows (gate/up: 128 gate + 128
 // up rows of the same output columns, so one tile owns exactly one
 // 128-column block of h and can quantise it in its epilogue).  With 192 rows
@@ -13,8 +15,7 @@
 //
 // Scales: the tile's row scales and weight-column scales for every k-block
 // are copied to LDS once per tile with 4-byte direct loads over contiguous
-// runs, row-major with a fixed row stride.
-// Row (activation) scales are powers of two, so the scaled MFMA
+// runs, row-major with a fixed row stride.  Row (activation) scales are powers of two, so the scaled MFMA
 // v_mfma_scale_f32_16x16x128_f8f6f4 applies them itself, exactly, as E8M0
 // bytes (lane l gives the scale of the row it feeds, l % 16, for its 32-byte
 // slice l / 16 of the block).  With arbitrary fp32 weight scales the block
