@@ -27,7 +27,14 @@ namespace {
 
 constexpr int BKB = 128;          // bytes (= fp8 elements) per k-step
 
-template <int BM, int BN, int WMW, int WNW, bool GATED>
+constexpr int kTabKB = 32;        // scale blocks per row the E8M0 weight-scale table holds
+
+// PO2W: the weight scales are powers of two.  Then a tile's weight-row scales
+// for every k-block are staged once, as E8M0 bytes, in an LDS table
+// (coalesced loads of the contiguous scale runs) instead of one scattered
+// 4-byte load per weight row and k-step, and the scaled MFMA applies both
+// scales and accumulates in place.
+template <int BM, int BN, int WMW, int WNW, bool GATED, bool PO2W>
 __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArgs p) {
     constexpr int NT = 64 * WMW * WNW;
     constexpr int FM = BM / 16 / WMW;
@@ -35,7 +42,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
     constexpr int FN = WN / 16;
     constexpr int BNO = GATED ? BN / 2 : BN;
     static_assert(FM >= 1 && FN >= 1 && (!GATED || (FN % 2 == 0 && BNO == 128)), "tile shape");
-    static_assert(BM + BN <= NT, "scale loads use disjoint thread ranges");
+    static_assert(BM <= NT && BN <= NT, "one row scale and one column scale per thread and k-block");
     constexpr int A_IT = (BM * 8 + NT - 1) / NT;
     constexpr int B_IT = (BN * 8 + NT - 1) / NT;
 
@@ -43,6 +50,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
     __shared__ uint4 sB[BN * 8];
     __shared__ float sAs[BM];
     __shared__ float sBs[BN];
+    __shared__ uint8_t sBe[PO2W ? BN * kTabKB : 4];     // [weight row][k-block] E8M0
     __shared__ float s_amax[WNW][BM];
     __shared__ int s_pre[kMaxExperts + 1];
     __shared__ int s_tmp[NT / kWave];
@@ -71,6 +79,17 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
         const uint8_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
         const float* wgs = p.w0_scales + (size_t)j * N * nbK;
         const float* wus = GATED ? p.w1_scales + (size_t)j * N * nbK : nullptr;
+
+        if constexpr (PO2W) {
+            __syncthreads();                       // the previous tile's reads of sBe are done
+            for (int e = tid; e < BN * nbK; e += NT) {
+                const int c = e / nbK, k = e - c * nbK;
+                const bool up = GATED && c >= BN / 2;
+                const int col = col0 + (up ? c - BN / 2 : c);
+                const float* sp = up ? wus : wgs;
+                sBe[c * kTabKB + k] = (uint8_t)(col < N ? e8m0_of_pow2(sp[(size_t)col * nbK + k]) : 127);
+            }
+        }
 
         uint4 ra[A_IT], rb[B_IT];
         float ras = 0.f, rbs = 0.f;
@@ -116,7 +135,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
                 ras = (tid < nvalid) ? p.a_scales[(size_t)(row0 + tid) * nbK + kb] : 0.f;
             }
             const int bt = tid - (NT - BN);           // the last BN threads load column scales
-            if (bt >= 0 && bt < BN) {
+            if (!PO2W && bt >= 0 && bt < BN) {
                 int col;
                 const float* sp;
                 if (GATED) {
@@ -145,7 +164,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
             }
             if (tid < BM) sAs[tid] = ras;
             const int bt = tid - (NT - BN);
-            if (bt >= 0 && bt < BN) sBs[bt] = rbs;
+            if (!PO2W && bt >= 0 && bt < BN) sBs[bt] = rbs;
         };
 
         floatx4 acc[FM][FN];
@@ -179,6 +198,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
             const int c0 = 2 * (lane >> 4);
             intx8 bfr[FN];
             float bsc[FN];
+            int sb8[FN];
 #pragma unroll
             for (int f = 0; f < FN; ++f) {
                 const int r = brow(f);
@@ -186,7 +206,8 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
                 const uint4 t1 = sB[r * 8 + ((c0 + 1) ^ (r & 7))];
                 bfr[f] = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
                                (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-                bsc[f] = sBs[r];
+                if constexpr (PO2W) sb8[f] = sBe[r * kTabKB + kb];
+                else bsc[f] = sBs[r];
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -197,17 +218,28 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
                     const uint4 t1 = sA[r * 8 + ((c0 + 1) ^ (r & 7))];
                     const intx8 afr = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
                                             (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-                    float asc[4];
+                    if constexpr (PO2W) {
+                        // the power-of-two scale of the row this lane feeds, and of
+                        // each weight row, as E8M0 bytes: the matrix core applies both
+                        const int sa8 = e8m0_of_pow2(sAs[r]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) asc[e] = sAs[mrow + (lane >> 4) * 4 + e];
+                        for (int f = 0; f < FN; ++f)
+                            if (fcol(f) < N)
+                                acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    afr, bfr[f], acc[i][f], 0, 0, 0, sa8, 0, sb8[f]);
+                    } else {
+                        float asc[4];
 #pragma unroll
-                    for (int f = 0; f < FN; ++f) {
-                        if (fcol(f) < N) {
-                            const floatx4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                            // lane l's outputs sit in column l % 16, whose scale bsc[f] holds
+                        for (int e = 0; e < 4; ++e) asc[e] = sAs[mrow + (lane >> 4) * 4 + e];
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[e], asc[e] * bsc[f], acc[i][f][e]);
+                        for (int f = 0; f < FN; ++f) {
+                            if (fcol(f) < N) {
+                                const floatx4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    afr, bfr[f], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                                // lane l's outputs sit in column l % 16, whose scale bsc[f] holds
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) acc[i][f][e] = fmaf(part[e], asc[e] * bsc[f], acc[i][f][e]);
+                            }
                         }
                     }
                 }
@@ -287,10 +319,10 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
     }
 }
 
-template <int BM, int BN, int WMW, int WNW, bool GATED>
+template <int BM, int BN, int WMW, int WNW, bool GATED, bool PO2W>
 hipError_t launch_cfg(const FfnArgs& a, hipStream_t stream) {
     static int per_cu = 0;
-    return launch_persistent(grouped_gemm_fp8_kernel<BM, BN, WMW, WNW, GATED>, 64 * WMW * WNW, a,
+    return launch_persistent(grouped_gemm_fp8_kernel<BM, BN, WMW, WNW, GATED, PO2W>, 64 * WMW * WNW, a,
                              stream, &per_cu);
 }
 
@@ -314,8 +346,17 @@ hipError_t launch_ffn_fp8(const FfnArgs& a, bool gated, hipStream_t stream) {
             return gated ? launch_wide<true, true>(a, stream) : launch_wide<false, true>(a, stream);
         return gated ? launch_wide<true, false>(a, stream) : launch_wide<false, false>(a, stream);
     }
-    return gated ? launch_cfg<128, 256, 2, 4, true>(a, stream)
-                 : launch_cfg<128, 128, 2, 2, false>(a, stream);
+    if (a.w_scales_pow2 && nbK <= kTabKB && a.rows_hint < 8) {
+        // decode-sized experts (a few rows each): 16-row tiles of 256 threads,
+        // small enough (LDS and registers) for several workgroups per CU, with
+        // the weight-row scales staged once per tile (measured: +21% gate/up,
+        // +9% down at 4 rows per expert; at 16 or more rows the 128-row tiles
+        // below are faster)
+        return gated ? launch_cfg<16, 256, 1, 4, true, true>(a, stream)
+                     : launch_cfg<16, 128, 1, 4, false, true>(a, stream);
+    }
+    return gated ? launch_cfg<128, 256, 2, 4, true, false>(a, stream)
+                 : launch_cfg<128, 128, 2, 2, false, false>(a, stream);
 }
 
 }  // namespace moeep

@@ -33,6 +33,7 @@ SMALL = [
     wl.scaled(C["gptoss_fp8"], "fp8_wide_f32_wscales", seg_rows=(600,), E=8, K=2, H=640, I=384,
               w_scales="fp32"),
     wl.scaled(C["gptoss_fp8"], "fp8_decode_real_dims", seg_rows=(24,), E=16, K=4),
+    wl.scaled(C["gptoss_fp8"], "fp8_decode_real_dims_f32_wscales", seg_rows=(24,), E=16, K=4, w_scales="fp32"),
     # H = I = 2880: 23 scale blocks per row (whole-row scale runs) and a 64-wide K tail,
     # 48 rows per expert (the wide fp8 tiles), both weight-scale conventions
     wl.scaled(C["gptoss_fp8"], "fp8_wide_real_dims", seg_rows=(192,), E=8, K=2),
@@ -82,11 +83,12 @@ def _forced_case(cfg, logits):
     return case
 
 
-@pytest.mark.parametrize("act,T", [("bf16", 300), ("bf16", 600), ("fp8", 300), ("fp8", 600)])
+@pytest.mark.parametrize("act,T", [("bf16", 300), ("bf16", 600), ("fp8", 40), ("fp8", 300), ("fp8", 600)])
 def test_all_tokens_one_expert_rest_empty(act, T):
     """All rows on one expert (several m-tiles of the 128-row and of the
-    256-row kernels, split evenly; for fp8 at T = 600 the 192-row wide
-    tiles), seven experts empty."""
+    256-row kernels, split evenly; for fp8 at T = 40 the 16-row tiles with
+    staged weight-scale bytes, at T = 600 the 192-row wide tiles), seven
+    experts empty."""
     base = C["dsv3_prefill"] if act == "bf16" else C["gptoss_fp8"]
     cfg = wl.scaled(base, f"one_expert_{act}_{T}", seg_rows=(T,), E=8, K=1, H=256, I=192)
     lg = np.random.default_rng(0).normal(size=(T, 8)).astype(np.float32)
