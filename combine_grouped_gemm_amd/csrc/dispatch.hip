@@ -6,20 +6,39 @@
 // source ranks (segments), as in the data-parallel attention setting of the
 // same post's "What we have to do".
 //
-// One block per (source token, slice of 256 16-byte vectors of its row): each
+// One block per (source token, slice of up to 448 16-byte vectors of its
+// row; a row of at most 448 vectors is one block of whole waves): each
 // thread reads one vector from HBM once and writes it to every local
 // destination row of the token, so a decode-sized batch still spreads over
-// the whole chip.  Plain stores: the non-temporal hint made this kernel
-// slower in the layer's sequence.  For fp8 storage the token is quantised once per
+// the whole chip.  A token with no slot on the local experts is not read at
+// all.  Plain stores: the non-temporal hint made this kernel slower in the
+// layer's sequence.  For fp8 storage the token is quantised once per
 // 128-element block (the 16 lanes of a DPP row cover a block; amax by
-// cross-lane moves inside the row) and every copy receives the same codes and scale.
+// cross-lane moves inside the row) and every copy receives the same codes
+// and scale.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace moeep {
 namespace {
 
-constexpr int kDispThreads = 448;      // one 16-byte source vector per thread (7 waves: a 7168-element bf16 row is two blocks)
+constexpr int kDispThreads = 448;      // most threads per block (7 waves: a 7168-element bf16 row is two blocks)
+
+// Threads per block for rows of nvec 16-byte vectors: whole waves, at most
+// kDispThreads; a multiple of 16 lanes, so fp8 scale blocks never straddle blocks.
+inline int dispatch_threads(int nvec) {
+    const int w = (nvec + kWave - 1) / kWave * kWave;
+    return w < kDispThreads ? w : kDispThreads;
+}
+
+// Whether token t has a slot on the local experts (uniform over the block).
+__device__ __forceinline__ bool has_local_slot(const int32_t* rows, int K, int cap) {
+    for (int k = 0; k < K; ++k) {
+        const int r = rows[k];
+        if (r >= 0 && r < cap) return true;
+    }
+    return false;
+}
 
 __device__ __forceinline__ const void* token_row(const SegTable& seg, int t, size_t row_bytes) {
     int i = 0;
@@ -32,11 +51,11 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_copy_kernel(
     SegTable seg, size_t row_bytes, const int32_t* __restrict__ row_of, int K, int cap,
     char* __restrict__ xd) {
     const int t = blockIdx.x;
-    const int c = blockIdx.y * kDispThreads + threadIdx.x;
+    const int c = blockIdx.y * blockDim.x + threadIdx.x;
     const int nvec = (int)(row_bytes / 16);
-    if (c >= nvec) return;
-    const uint4 v = static_cast<const uint4*>(token_row(seg, t, row_bytes))[c];
     const int32_t* rows = row_of + (size_t)t * K;
+    if (c >= nvec || !has_local_slot(rows, K, cap)) return;
+    const uint4 v = static_cast<const uint4*>(token_row(seg, t, row_bytes))[c];
     for (int k = 0; k < K; ++k) {
         const int r = rows[k];
         if (r >= 0 && r < cap) reinterpret_cast<uint4*>(xd + (size_t)r * row_bytes)[c] = v;
@@ -50,9 +69,11 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
     SegTable seg, int H, const int32_t* __restrict__ row_of, int K, int cap,
     uint8_t* __restrict__ xd, float* __restrict__ xd_scales) {
     const int t = blockIdx.x;
-    const int c = blockIdx.y * kDispThreads + threadIdx.x;
+    const int c = blockIdx.y * blockDim.x + threadIdx.x;
     const int nvec = H / 8;                 // 8 bf16 per 16-byte vector
     const int nblk = (H + 127) / 128;
+    const int32_t* rows = row_of + (size_t)t * K;
+    if (!has_local_slot(rows, K, cap)) return;      // whole block: the DPP rows below stay complete
     const bool ok = c < nvec;
     const uint4* src = static_cast<const uint4*>(token_row(seg, t, (size_t)H * 2));
     const uint4 v = ok ? src[c] : make_uint4(0, 0, 0, 0);
@@ -65,12 +86,9 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
     if (!ok) return;
     const float s = pow2_block_scale(amax);
     const float rs = 1.0f / s;               // exact: s is a power of two
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3_sat(f[i] * rs) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3_sat(f[4 + i] * rs) << (8 * i);
-    const int32_t* rows = row_of + (size_t)t * K;
+    // |f * rs| <= amax / s <= 448, the range where the hardware conversion is exact RNE
+    const uint32_t lo = e4m3_pair(f[0] * rs, f[1] * rs) | (e4m3_pair(f[2] * rs, f[3] * rs) << 16);
+    const uint32_t hi = e4m3_pair(f[4] * rs, f[5] * rs) | (e4m3_pair(f[6] * rs, f[7] * rs) << 16);
     for (int k = 0; k < K; ++k) {
         const int r = rows[k];
         if (r < 0 || r >= cap) continue;
@@ -87,12 +105,14 @@ hipError_t launch_dispatch(const SegTable& seg, int B, int H, int kind, const in
     if (kind == 0 || kind == 1) {
         const size_t row_bytes = (size_t)H * (kind == 0 ? 4 : 2);
         const int nvec = (int)(row_bytes / 16);
-        dim3 grid(B, (nvec + kDispThreads - 1) / kDispThreads);
-        hipLaunchKernelGGL(dispatch_copy_kernel, grid, dim3(kDispThreads), 0, stream, seg,
+        const int nt = dispatch_threads(nvec);
+        dim3 grid(B, (nvec + nt - 1) / nt);
+        hipLaunchKernelGGL(dispatch_copy_kernel, grid, dim3(nt), 0, stream, seg,
                            row_bytes, row_of, K, cap, static_cast<char*>(xd));
     } else {
-        dim3 grid(B, (H / 8 + kDispThreads - 1) / kDispThreads);
-        hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kDispThreads), 0, stream, seg, H,
+        const int nt = dispatch_threads(H / 8);
+        dim3 grid(B, (H / 8 + nt - 1) / nt);
+        hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(nt), 0, stream, seg, H,
                            row_of, K, cap, static_cast<uint8_t*>(xd), xd_scales);
     }
     return hipGetLastError();
