@@ -99,6 +99,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     __shared__ uint4 sa1[BM * CPR];
     __shared__ uint4 sb1[BN * CPR];
     __shared__ int s_pre[kMaxExperts + 1];
+    __shared__ uint16_t s_ord[kMaxExperts];          // experts, most rows first
+    static_assert(sizeof(sa0) >= kMaxExperts * sizeof(int), "row counts fit in the first row stage");
     __shared__ int s_tmp[NT / kWave];
 
     auto a_base = [&](auto I) -> char* {
@@ -116,7 +118,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
     const int nk = Kdim / BK;
 
-    build_tile_prefix<NT, BM>(p, s_pre, s_tmp);
+    // largest experts' tiles first; the first row stage is free scratch until the first load
+    build_tile_prefix_sorted<NT, BM>(p, s_pre, s_ord, reinterpret_cast<int*>(sa0), s_tmp);
     const int n_tiles_n = (N + BNO - 1) / BNO;
     const int total = n_tiles_n * s_pre[p.E_loc];
     const int G = gridDim.x;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     uint16_t* __restrict__ Out = static_cast<uint16_t*>(p.out);
 
     for (int tau = v; tau < total; tau += G) {
-        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p);
+        const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p, s_ord);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
         const uint16_t* wg = W0 + (size_t)j * N * Kdim;

@@ -78,6 +78,8 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     __shared__ float s_as[BM * SK];
     __shared__ float s_bs[BN * SK];
     __shared__ int s_pre[kMaxExperts + 1];
+    __shared__ uint16_t s_ord[kMaxExperts];          // experts, most rows first
+    static_assert(sizeof(sa0) >= kMaxExperts * sizeof(int), "row counts fit in the first row stage");
     __shared__ int s_tmp[NT / kWave];
 
     auto a_base = [&](auto I) -> char* {
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     const bool k_tail = nk * ROWB != Kdim;          // last block holds 64 bytes
     const int nbN = (N + 127) / 128;
 
-    build_tile_prefix<NT, BM>(p, s_pre, s_tmp);
+    // largest experts' tiles first; the first row stage is free scratch until the first load
+    build_tile_prefix_sorted<NT, BM>(p, s_pre, s_ord, reinterpret_cast<int*>(sa0), s_tmp);
     const int n_tiles_n = (N + BNO - 1) / BNO;
     const int total = n_tiles_n * s_pre[p.E_loc];
     const int G = gridDim.x;
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     // w, w + NW, ... of a stage (8 rows each; row blocks first, then weight
     // blocks); rows / columns past the valid ones re-read row 0.
     auto stage_tile = [&](int t) -> TileCoord {
-        const TileCoord tc = decode_tile<BM>(t, n_tiles_n, s_pre, p);
+        const TileCoord tc = decode_tile<BM>(t, n_tiles_n, s_pre, p, s_ord);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
         const float* wgs = p.w0_scales + (size_t)j * N * nk;

@@ -3,12 +3,13 @@
 // The per-expert row counts exist only on the device (offsets of the
 // contiguous layout, or the valid-row counts of the masked layout), so a
 // persistent grid derives its work list there: every block builds the
-// prefix sum over local experts of ceil(rows / BM) m-tiles in LDS and maps a
-// linear tile index tau to (expert j, n-tile, m-tile) by binary search, with
-// the m-tile index fastest so that tiles sharing one weight tile are
-// consecutive.  An expert's rows are split evenly over its m-tiles.  Blocks are renumbered XCD-major (hardware dispatch places
-// block b on XCD b % 8), so consecutive tile indices run on one XCD and
-// share its L2.
+// prefix sum over local experts (in id order, or most rows first) of
+// ceil(rows / BM) m-tiles in LDS and maps a linear tile index tau to
+// (expert j, n-tile, m-tile) by binary search, with the m-tile index fastest
+// so that tiles sharing one weight tile are consecutive.  An expert's rows
+// are split evenly over its m-tiles.  Blocks are renumbered XCD-major
+// (hardware dispatch places block b on XCD b % 8), so consecutive tile
+// indices run on one XCD and share its L2.
 #pragma once
 
 #include "device_common.hpp"
@@ -34,23 +35,17 @@ __device__ __forceinline__ void expert_rows(const FfnArgs& p, int j, int& r0, in
     }
 }
 
-// Block-wide exclusive prefix of m-tile counts per expert into s_pre[0..E_loc].
+// Block-wide exclusive prefix into s_pre[0..n] of count(i), i in [0, n).
 // s_tmp needs NT / 64 ints.  Ends with a barrier.
-template <int NT, int BM>
-__device__ void build_tile_prefix(const FfnArgs& p, int* s_pre, int* s_tmp) {
-    const int E_loc = p.E_loc;
+template <int NT, typename Count>
+__device__ void scan_tile_counts(int n, Count count, int* s_pre, int* s_tmp) {
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
     constexpr int NW = NT / kWave;
     int carry = 0;
     if (tid == 0) s_pre[0] = 0;
-    for (int base = 0; base < E_loc; base += NT) {
+    for (int base = 0; base < n; base += NT) {
         const int j = base + tid;
-        int v = 0;
-        if (j < E_loc) {
-            int r0, r1;
-            expert_rows(p, j, r0, r1);
-            v = (r1 - r0 + BM - 1) / BM;
-        }
+        const int v = j < n ? count(j) : 0;
         int x = v;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
@@ -65,11 +60,52 @@ __device__ void build_tile_prefix(const FfnArgs& p, int* s_pre, int* s_tmp) {
             wsum += (w < wv) ? s_tmp[w] : 0;
             total += s_tmp[w];
         }
-        if (j < E_loc) s_pre[j + 1] = carry + wsum + x;
+        if (j < n) s_pre[j + 1] = carry + wsum + x;
         carry += total;
         __syncthreads();
     }
     __syncthreads();
+}
+
+// Block-wide exclusive prefix of m-tile counts per expert into s_pre[0..E_loc],
+// experts in id order.  s_tmp needs NT / 64 ints.  Ends with a barrier.
+template <int NT, int BM>
+__device__ void build_tile_prefix(const FfnArgs& p, int* s_pre, int* s_tmp) {
+    scan_tile_counts<NT>(p.E_loc, [&](int j) {
+        int r0, r1;
+        expert_rows(p, j, r0, r1);
+        return (r1 - r0 + BM - 1) / BM;
+    }, s_pre, s_tmp);
+}
+
+// The same prefix with the experts in decreasing row count (ties: lower id
+// first): s_ord[pos] is the expert at position pos, s_pre the prefix in that
+// order.  A persistent grid walks tiles in this order, so its last, partly
+// filled round holds the smallest experts' tiles instead of whichever
+// experts have the highest ids (longest tiles first).  s_rows is E_loc ints
+// of scratch that is free at this point.  Ends with a barrier.
+template <int NT, int BM>
+__device__ void build_tile_prefix_sorted(const FfnArgs& p, int* s_pre, uint16_t* s_ord, int* s_rows,
+                                         int* s_tmp) {
+    const int E_loc = p.E_loc, tid = threadIdx.x;
+    for (int j = tid; j < E_loc; j += NT) {
+        int r0, r1;
+        expert_rows(p, j, r0, r1);
+        s_rows[j] = r1 - r0;
+    }
+    __syncthreads();
+    for (int j = tid; j < E_loc; j += NT) {
+        const int r = s_rows[j];
+        int rank = 0;
+        for (int i = 0; i < E_loc; ++i) {
+            const int q = s_rows[i];
+            rank += (q > r || (q == r && i < j)) ? 1 : 0;
+        }
+        s_ord[rank] = (uint16_t)j;
+    }
+    __syncthreads();
+    scan_tile_counts<NT>(E_loc, [&](int pos) { return (s_rows[s_ord[pos]] + BM - 1) / BM; }, s_pre,
+                         s_tmp);
 }
 
 struct TileCoord {
@@ -79,22 +115,24 @@ struct TileCoord {
     int nvalid;   // valid rows in the tile (<= BM)
 };
 
+// s_ord: expert at each prefix position (build_tile_prefix_sorted), or nullptr
+// for id order.
 template <int BM>
 __device__ __forceinline__ TileCoord decode_tile(int tau, int n_tiles_n, const int* s_pre,
-                                                 const FfnArgs& p) {
-    int lo = 0, hi = p.E_loc;     // largest j with n_tiles_n * s_pre[j] <= tau
+                                                 const FfnArgs& p, const uint16_t* s_ord = nullptr) {
+    int lo = 0, hi = p.E_loc;     // largest position j with n_tiles_n * s_pre[j] <= tau
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (n_tiles_n * s_pre[mid] <= tau) lo = mid; else hi = mid;
     }
     TileCoord t;
-    t.j = lo;
+    t.j = s_ord != nullptr ? (int)s_ord[lo] : lo;
     const int mt_j = s_pre[lo + 1] - s_pre[lo];
     const int local = tau - n_tiles_n * s_pre[lo];
     t.nt = local / mt_j;
     const int mt = local % mt_j;
     int r0, r1;
-    expert_rows(p, lo, r0, r1);
+    expert_rows(p, t.j, r0, r1);
     // balanced split: m-tile mt of mt_j takes rows [n*mt/mt_j, n*(mt+1)/mt_j) of the
     // expert, at most ceil(n/mt_j) <= BM of them
     const int n = r1 - r0;
