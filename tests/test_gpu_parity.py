@@ -41,6 +41,11 @@ SMALL = [
     # fp8 at DeepSeek dimensions: 56 scale blocks per row (past the wide tiles' scale table),
     # ~32 rows per expert through the 128-row fp8 tiles
     wl.scaled(C["gptoss_fp8"], "fp8_dsv3_dims", seg_rows=(64,), E=16, K=8, H=7168, I=2048),
+    # 600 local experts (10..165 rows each) through the wide tiles: more experts than the
+    # kernels' 512 threads, so the largest-first expert ranking and the tile prefix take
+    # several passes
+    wl.scaled(C["dsv3_prefill"], "prefill_many_experts", seg_rows=(4800,), E=600, K=8, H=128, I=64),
+    wl.scaled(C["gptoss_fp8"], "fp8_wide_many_experts", seg_rows=(3600,), E=600, K=8, H=256, I=128),
 ]
 
 
