@@ -132,7 +132,7 @@ size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 size_t ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt) {
     if (cap_rows < 0 || I < 1) return 0;
     size_t bytes = round256((size_t)cap_rows * I * elem_size(act_dt));
-    if (act_dt == MOE_FP8_E4M3) bytes += round256((size_t)cap_rows * ((I + 127) / 128) * sizeof(float));
+    if (act_dt == MOE_FP8_E4M3) bytes += round256((size_t)cap_rows * (((size_t)I + 127) / 128) * sizeof(float));
     return bytes;
 }
 
@@ -246,14 +246,20 @@ moe_status_t moe_eplb_place(const int64_t* load, int E, int n_groups, int32_t* p
     REQUIRE(n_groups >= 1 && E % n_groups == 0, "n_groups must divide E (got E=%d, n_groups=%d)", E,
             n_groups);
     REQUIRE(load && phys_of_logical, "null load or phys_of_logical");
-    for (int e = 0; e < E; ++e) REQUIRE(load[e] >= 0, "load[%d] < 0", e);
+    int64_t total = 0;     // group totals and their differences stay within it
+    for (int e = 0; e < E; ++e) {
+        REQUIRE(load[e] >= 0, "load[%d] < 0", e);
+        REQUIRE(load[e] <= INT64_MAX - total, "the loads' total must fit in int64");
+        total += load[e];
+    }
     moeep::place_experts(load, E, n_groups, phys_of_logical);
     g_last_error[0] = '\0';
     return MOE_OK;
 }
 
 size_t moe_layout_workspace_bytes(int B, int K, int E) {
-    if (B < 0 || K < 1 || E < 1) return 0;
+    // 0 for sizes moe_layout rejects (B * K past int32 included)
+    if (B < 0 || K < 1 || E < 1 || (long long)B * K > 0x7fffffffLL) return 0;
     return moeep::layout_workspace_bytes(B, K, E);
 }
 

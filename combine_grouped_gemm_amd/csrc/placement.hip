@@ -52,7 +52,7 @@ bool place_experts(const int64_t* load, int E, int G, int32_t* phys_of_logical) 
             for (int b : B) {
                 const long long d = load[a] - load[b];
                 if (d <= 0 || d >= diff) continue;
-                const long long score = std::llabs(diff - 2 * d);
+                const long long score = std::llabs((diff - d) - d);   // |diff - 2d| without overflow
                 if (best_score < 0 || score < best_score) {
                     best_score = score;
                     best_a = a;

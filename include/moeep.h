@@ -46,14 +46,20 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status and dtype codes are plain 32-bit integers with named values, so
+   every value a caller passes (an unknown dtype code, an out-of-range
+   status for moe_status_string) is well defined and gets a status or a
+   string back. */
+typedef int32_t moe_status_t;
+enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,   /* a pointer, size or alignment check failed */
     MOE_ERR_UNSUPPORTED = 2,   /* a valid but unimplemented dtype/shape combination */
     MOE_ERR_HIP = 3            /* a kernel launch failed */
-} moe_status_t;
+};
 
-typedef enum {
+typedef int32_t moe_dtype_t;
+enum {
     MOE_F32 = 0,
     MOE_BF16 = 1,
     MOE_FP8_E4M3 = 2,          /* OCP e4m3fn (finite max 448), with fp32 1x128 block scales */
@@ -61,7 +67,7 @@ typedef enum {
                                   of two 2^e, e in [-127, 127] (the E8M0 scale convention of
                                   the microscaling formats); the matrix cores apply such
                                   scales, and only a scale's exponent field is read */
-} moe_dtype_t;
+};
 
 /* Largest number of simulated source segments moe_dispatch accepts. */
 #define MOE_MAX_SEGMENTS 64
@@ -153,10 +159,12 @@ moe_status_t moe_route_shared(const float* logits, int B, int E, int K, int n_sh
  * the most and the least loaded sets differ, the swap between them whose load
  * difference d (0 < d < gap) is closest to gap/2 is made (ties: lower ids);
  * ids inside a set ascend with the logical id.
- *   load  (E) int64 host, >= 0: activation counts (e.g. summed moe_layout counts).
+ *   load  (E) int64 host, >= 0, total <= INT64_MAX: activation counts (e.g.
+ *         summed moe_layout counts).
  *   phys_of_logical (E) int32 host out.
  * Returns MOE_ERR_INVALID_ARG for E outside [1, 1024], n_groups not dividing
- * E, a negative load or null pointers.
+ * E, a negative load, loads whose total does not fit in int64, or null
+ * pointers.
  */
 moe_status_t moe_eplb_place(const int64_t* load, int E, int n_groups, int32_t* phys_of_logical);
 
