@@ -46,6 +46,9 @@ SMALL = [
     # several passes
     wl.scaled(C["dsv3_prefill"], "prefill_many_experts", seg_rows=(4800,), E=600, K=8, H=128, I=64),
     wl.scaled(C["gptoss_fp8"], "fp8_wide_many_experts", seg_rows=(3600,), E=600, K=8, H=256, I=128),
+    # more than 8 slots per token: combine gathers in passes of 8 slots (two and three passes)
+    wl.scaled(C["dsv3_decode"], "decode_k12", seg_rows=(48,), E=32, K=12, H=256, I=128),
+    wl.scaled(C["dsv3_prefill"], "prefill_k20", seg_rows=(40,), E=64, K=20, H=128, I=64),
 ]
 
 
