@@ -298,7 +298,7 @@ def cpu_baseline(cfg, x_cpu, logits_cpu, weights, budget_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "libmoeep runs on one GPU only (no multi-GPU path); --gpus must be 1"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
