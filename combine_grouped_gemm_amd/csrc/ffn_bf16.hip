@@ -67,7 +67,9 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
     const uint16_t* __restrict__ W1 = static_cast<const uint16_t*>(p.w1);
     uint16_t* __restrict__ Out = static_cast<uint16_t*>(p.out);
 
-    for (int tau = v; tau < total; tau += G) {
+    for (int rnd = 0;; ++rnd) {
+        const int tau = round_tile(rnd, v, blockIdx.x, G, total);
+        if (tau < 0) break;
         const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;

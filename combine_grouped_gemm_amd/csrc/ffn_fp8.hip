@@ -71,7 +71,9 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
     const uint8_t* __restrict__ W0 = static_cast<const uint8_t*>(p.w0);
     const uint8_t* __restrict__ W1 = static_cast<const uint8_t*>(p.w1);
 
-    for (int tau = v; tau < total; tau += G) {
+    for (int rnd = 0;; ++rnd) {
+        const int tau = round_tile(rnd, v, blockIdx.x, G, total);
+        if (tau < 0) break;
         const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;

@@ -147,6 +147,22 @@ __device__ __forceinline__ TileCoord decode_tile(int tau, int n_tiles_n, const i
     return t;
 }
 
+// Tile of round r for the block with XCD-major position v and hardware
+// index b in a grid of G, or -1 when it has none.  Rounds go in XCD-major
+// order (tiles that run together are neighbours in memory and share L2),
+// except a last round that fills less than half the grid: in XCD-major
+// order it would run on the first few XCDs alone, so it goes in hardware
+// order, spread over all of them.  (Measured on the decode-sized FFN with
+// several blocks per CU: spreading a 45%-full last round 5% faster overall,
+// a 78%-full one 2.7% slower.)
+__device__ __forceinline__ int round_tile(int r, int v, int b, int G, int total) {
+    const long long base = (long long)r * G;
+    if (base >= total) return -1;
+    const long long rem = total - base;
+    const int tau = (int)base + (2 * rem >= G ? v : b);
+    return tau < total ? tau : -1;
+}
+
 // XCD-major renumbering of the block index (identity when G % 8 != 0).
 __device__ __forceinline__ int xcd_block_order() {
     const int G = gridDim.x, b = blockIdx.x;
