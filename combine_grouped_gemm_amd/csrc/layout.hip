@@ -23,6 +23,14 @@
 //             same expert, which keeps rows of an expert in ascending slot
 //             order.  Also fills src_of's padding rows with -1.
 //
+// A batch of at most kFusedMaxSlots slots (decode sizes) takes one launch
+// instead: a single 1024-thread workgroup counts every expert (match masks
+// and LDS atomics, order-independent), scans the local counts into the
+// offsets, then ranks the slots 1024 at a time -- a slot's row is its
+// expert's running base plus the same-expert slots of the lower waves of
+// its chunk plus the lower lanes of its own wave -- which gives the same
+// stable rows as the three kernels without their launch gaps.
+//
 // The fixed-capacity ("masked") variant (SGLang "Expert Parallelism", the
 // MoE-runner table: masked layout for decode) runs the same three kernels;
 // local expert j owns rows [j*cap_e, (j+1)*cap_e), so the ranking needs no
@@ -177,6 +185,96 @@ __global__ __launch_bounds__(kWave) void layout_rank_kernel(
     }
 }
 
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedMaxSlots = 4096;
+constexpr int kFusedMaxE = 1024;
+
+__global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
+    const int32_t* __restrict__ ids, int n_slots, int E, int e_begin, int e_end, int cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ src_of) {
+    __shared__ int s_cnt[kFusedMaxE];                  // all experts
+    __shared__ int s_next[kFusedMaxE];                 // local experts: next free row
+    __shared__ int s_wc[kFusedWaves * kFusedMaxE];     // [wave][local expert] slots in this chunk
+    __shared__ int s_tmp[kFusedWaves];
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int E_loc = e_end - e_begin;
+    const int nbits = id_bits(E);
+
+    for (int e = tid; e < E; e += kFusedThreads) s_cnt[e] = 0;
+    __syncthreads();
+    // counts over all experts
+    for (int s0 = 0; s0 < n_slots; s0 += kFusedThreads) {
+        const int s = s0 + tid;
+        const int e = s < n_slots ? ids[s] : -1;
+        const bool valid = e >= 0 && e < E;
+        const uint64_t active = ballot64(valid);
+        if (active != 0) {                             // wave-uniform
+            const uint64_t m = match_mask((uint32_t)(valid ? e : 0), active, nbits);
+            if (valid && (m & lanemask_lt()) == 0) atomicAdd(&s_cnt[e], popc64(m));
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kFusedThreads) counts[e] = s_cnt[e];
+    // offsets: exclusive scan of the local counts, one expert per thread
+    const int v = tid < E_loc ? s_cnt[e_begin + tid] : 0;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) s_tmp[wv] = x;
+    __syncthreads();
+    int wsum = 0, R = 0;
+#pragma unroll
+    for (int w = 0; w < kFusedWaves; ++w) {
+        wsum += w < wv ? s_tmp[w] : 0;
+        R += s_tmp[w];
+    }
+    if (tid < E_loc) {
+        const int off = wsum + x - v;
+        offsets[tid] = off;
+        s_next[tid] = off;
+    }
+    if (tid == 0) offsets[E_loc] = R;
+    // stable ranks, one chunk of kFusedThreads slots at a time
+    for (int s0 = 0; s0 < n_slots; s0 += kFusedThreads) {
+        for (int i = tid; i < kFusedWaves * E_loc; i += kFusedThreads) s_wc[i] = 0;
+        __syncthreads();
+        const int s = s0 + tid;
+        const int e = s < n_slots ? ids[s] : -1;
+        const bool local = e >= e_begin && e < e_end;
+        const uint64_t active = ballot64(local);
+        uint64_t m = 0;
+        if (active != 0) {                             // wave-uniform
+            m = match_mask((uint32_t)(local ? e - e_begin : 0), active, nbits);
+            if (local && (m & lanemask_lt()) == 0) s_wc[wv * E_loc + (e - e_begin)] = popc64(m);
+        }
+        __syncthreads();
+        int row = -1;
+        if (local) {
+            const int j = e - e_begin;
+            int r = s_next[j] + popc64(m & lanemask_lt());
+            for (int w = 0; w < wv; ++w) r += s_wc[w * E_loc + j];
+            row = r < cap ? r : -1;
+            if (row >= 0) src_of[row] = s;
+        }
+        if (s < n_slots) row_of[s] = row;
+        __syncthreads();
+        for (int j = tid; j < E_loc; j += kFusedThreads) {
+            int add = 0;
+#pragma unroll
+            for (int w = 0; w < kFusedWaves; ++w) add += s_wc[w * E_loc + j];
+            s_next[j] += add;
+        }
+        __syncthreads();                               // s_wc is read above before the next chunk clears it
+    }
+    // padding rows of src_of
+    for (int r = R + tid; r < cap; r += kFusedThreads) src_of[r] = -1;
+}
+
 }  // namespace
 
 size_t layout_workspace_bytes(int B, int K, int E) {
@@ -189,6 +287,11 @@ hipError_t launch_layout(const int32_t* ids, int B, int K, int E, int e_begin, i
                          int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
                          int cap, void* ws, hipStream_t stream) {
     const int n_slots = B * K;
+    if (n_slots <= kFusedMaxSlots && E <= kFusedMaxE) {
+        hipLaunchKernelGGL(layout_fused_kernel, dim3(1), dim3(kFusedThreads), 0, stream, ids, n_slots, E,
+                           e_begin, e_end, cap, counts, offsets, row_of, src_of);
+        return hipGetLastError();
+    }
     const int nchunk = n_chunks(n_slots);
     LayoutWs w = carve(ws, nchunk, E);
     if (nchunk > 0) {

@@ -49,6 +49,12 @@ SMALL = [
     # more than 8 slots per token: combine gathers in passes of 8 slots (two and three passes)
     wl.scaled(C["dsv3_decode"], "decode_k12", seg_rows=(48,), E=32, K=12, H=256, I=128),
     wl.scaled(C["dsv3_prefill"], "prefill_k20", seg_rows=(40,), E=64, K=20, H=128, I=64),
+    # the single-workgroup layout's limit: 4096 slots (four 1024-slot chunks) and just past
+    # it (the three-kernel layout), on a partial expert range
+    wl.scaled(C["ep8_share"], "layout_4096_slots", seg_rows=(300, 212), E=32, K=8, H=128, I=64,
+              e_begin=8, e_end=24),
+    wl.scaled(C["ep8_share"], "layout_4104_slots", seg_rows=(300, 213), E=32, K=8, H=128, I=64,
+              e_begin=8, e_end=24),
 ]
 
 
