@@ -23,8 +23,8 @@
 //             same expert, which keeps rows of an expert in ascending slot
 //             order.  Also fills src_of's padding rows with -1.
 //
-// A batch of at most kFusedMaxSlots slots (decode sizes) takes one launch
-// instead: a single 1024-thread workgroup counts every expert (match masks
+// A batch of at most kFusedMaxSlots slots (decode sizes), in either layout,
+// takes one launch instead: a single 1024-thread workgroup counts every expert (match masks
 // and LDS atomics, order-independent), scans the local counts into the
 // offsets, then ranks the slots 1024 at a time -- a slot's row is its
 // expert's running base plus the same-expert slots of the lower waves of
@@ -190,6 +190,9 @@ constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kFusedMaxSlots = 4096;
 constexpr int kFusedMaxE = 1024;
 
+// MASKED: cap is cap_e (rows per expert block), `offsets` receives m (valid
+// rows per local expert) and local expert j's rows start at j * cap_e.
+template <bool MASKED>
 __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
     const int32_t* __restrict__ ids, int n_slots, int E, int e_begin, int e_end, int cap,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
@@ -217,7 +220,8 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
     }
     __syncthreads();
     for (int e = tid; e < E; e += kFusedThreads) counts[e] = s_cnt[e];
-    // offsets: exclusive scan of the local counts, one expert per thread
+    // contiguous: offsets = exclusive scan of the local counts, one expert per thread;
+    // masked: m = counts clamped to the block, ranks start at 0 in every block
     const int v = tid < E_loc ? s_cnt[e_begin + tid] : 0;
     int x = v;
 #pragma unroll
@@ -235,10 +239,10 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
     }
     if (tid < E_loc) {
         const int off = wsum + x - v;
-        offsets[tid] = off;
-        s_next[tid] = off;
+        offsets[tid] = MASKED ? (v < cap ? v : cap) : off;
+        s_next[tid] = MASKED ? 0 : off;
     }
-    if (tid == 0) offsets[E_loc] = R;
+    if (!MASKED && tid == 0) offsets[E_loc] = R;
     // stable ranks, one chunk of kFusedThreads slots at a time
     for (int s0 = 0; s0 < n_slots; s0 += kFusedThreads) {
         for (int i = tid; i < kFusedWaves * E_loc; i += kFusedThreads) s_wc[i] = 0;
@@ -258,7 +262,10 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
             const int j = e - e_begin;
             int r = s_next[j] + popc64(m & lanemask_lt());
             for (int w = 0; w < wv; ++w) r += s_wc[w * E_loc + j];
-            row = r < cap ? r : -1;
+            if (MASKED)
+                row = r < cap ? j * cap + r : -1;
+            else
+                row = r < cap ? r : -1;
             if (row >= 0) src_of[row] = s;
         }
         if (s < n_slots) row_of[s] = row;
@@ -272,7 +279,14 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
         __syncthreads();                               // s_wc is read above before the next chunk clears it
     }
     // padding rows of src_of
-    for (int r = R + tid; r < cap; r += kFusedThreads) src_of[r] = -1;
+    if (MASKED) {
+        for (int r = tid; r < E_loc * cap; r += kFusedThreads) {
+            const int j = r / cap, q = r - j * cap;
+            if (q >= s_cnt[e_begin + j]) src_of[r] = -1;
+        }
+    } else {
+        for (int r = R + tid; r < cap; r += kFusedThreads) src_of[r] = -1;
+    }
 }
 
 }  // namespace
@@ -288,8 +302,8 @@ hipError_t launch_layout(const int32_t* ids, int B, int K, int E, int e_begin, i
                          int cap, void* ws, hipStream_t stream) {
     const int n_slots = B * K;
     if (n_slots <= kFusedMaxSlots && E <= kFusedMaxE) {
-        hipLaunchKernelGGL(layout_fused_kernel, dim3(1), dim3(kFusedThreads), 0, stream, ids, n_slots, E,
-                           e_begin, e_end, cap, counts, offsets, row_of, src_of);
+        hipLaunchKernelGGL(layout_fused_kernel<false>, dim3(1), dim3(kFusedThreads), 0, stream, ids, n_slots,
+                           E, e_begin, e_end, cap, counts, offsets, row_of, src_of);
         return hipGetLastError();
     }
     const int nchunk = n_chunks(n_slots);
@@ -310,6 +324,11 @@ hipError_t launch_layout_masked(const int32_t* ids, int B, int K, int E, int e_b
                                 int32_t* counts, int32_t* m, int32_t* row_of, int32_t* src_of,
                                 int cap_e, void* ws, hipStream_t stream) {
     const int n_slots = B * K;
+    if (n_slots <= kFusedMaxSlots && E <= kFusedMaxE) {
+        hipLaunchKernelGGL(layout_fused_kernel<true>, dim3(1), dim3(kFusedThreads), 0, stream, ids, n_slots,
+                           E, e_begin, e_end, cap_e, counts, m, row_of, src_of);
+        return hipGetLastError();
+    }
     const int nchunk = n_chunks(n_slots);
     LayoutWs w = carve(ws, nchunk, E);
     if (nchunk > 0) {
