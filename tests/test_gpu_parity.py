@@ -55,6 +55,11 @@ SMALL = [
               e_begin=8, e_end=24),
     wl.scaled(C["ep8_share"], "layout_4104_slots", seg_rows=(300, 213), E=32, K=8, H=128, I=64,
               e_begin=8, e_end=24),
+    # degenerate shapes: one expert (every gate 1), one token, empty source segments
+    wl.scaled(C["dsv3_prefill"], "single_expert", seg_rows=(37,), E=1, K=1, H=128, I=64),
+    wl.scaled(C["dsv3_decode"], "single_token", seg_rows=(1,), E=8, K=2, H=128, I=64),
+    wl.scaled(C["ep8_share"], "empty_segments", seg_rows=(0, 7, 0, 0, 5, 0), E=16, K=3, H=128, I=64,
+              e_begin=2, e_end=9),
 ]
 
 
