@@ -7,8 +7,8 @@
 // One wave per token.  Lane l keeps logits l, l+64, ... in registers as
 // order-preserving 64-bit keys (value in the high word, inverted expert id
 // in the low word), so one unsigned max selects the largest logit with the
-// lowest id.  K rounds of "local max -> wave max by xor shuffles -> owner
-// clears its key" produce the picks in order; gates come from the selected
+// lowest id.  K rounds of "local max -> wave max (DPP row reductions, then
+// one lane per row) -> owner clears its key" produce the picks in order; gates come from the selected
 // values with fp32 expf, written coalesced at the end.  With a placement map
 // (Moreh report, load balancing between GPUs: the router emits the renumbered
 // expert ids) the chosen ids are written through it; selection and gates are
@@ -33,11 +33,33 @@ __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_xor(lo, m, kWave);
-    hi = __shfl_xor(hi, m, kWave);
+// 64-bit key of the lane that DPP control CTRL names within this lane's row
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
     return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the wave, the same in every lane: within each 16-lane DPP row
+// by cross-lane moves in the VALU (partners lane ^ 1, lane ^ 2, then the
+// half-row and row mirrors, as in row16_max), then across the four rows by
+// reading one lane of each.  No LDS traffic, unlike a shuffle.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_u64(v, dpp_u64<0xB1>(v));
+    v = max_u64(v, dpp_u64<0x4E>(v));
+    v = max_u64(v, dpp_u64<0x141>(v));
+    v = max_u64(v, dpp_u64<0x140>(v));
+    return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                   max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
 template <int EPL>
@@ -66,11 +88,7 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
         uint64_t best = key[0];
 #pragma unroll
         for (int j = 1; j < EPL; ++j) best = key[j] > best ? key[j] : best;
-#pragma unroll
-        for (int m = 1; m < kWave; m <<= 1) {
-            uint64_t o = shfl_xor_u64(best, m);
-            best = o > best ? o : best;
-        }
+        best = wave_max_u64(best);
         const int e = (int)(0xffffffffu - (uint32_t)best);
         const float v = key_value((uint32_t)(best >> 32));
         if (k == 0) top = v;
