@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     int K, int H, int cap, void* __restrict__ out) {
     const int t = blockIdx.x;
     const int nvec = H / 8;
-    const int c = blockIdx.y * kCombThreads + threadIdx.x;
+    const int c = blockIdx.y * blockDim.x + threadIdx.x;
     if (c >= nvec) return;
     const int32_t* rows = row_of + (size_t)t * K;
     const float* gates = w + (size_t)t * K;
@@ -86,7 +86,13 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 hipError_t launch_combine(const void* y, int kind, const int32_t* row_of, const float* w, int B,
                           int K, int H, void* out, int cap, hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    dim3 grid(B, (H / 8 + kCombThreads - 1) / kCombThreads), block(kCombThreads);
+    // slices of at most kCombThreads vectors, balanced (a 360-vector row is two
+    // slices of 180, not 256 + 104), in whole waves
+    const int nvec = H / 8;
+    const int nslice = (nvec + kCombThreads - 1) / kCombThreads;
+    const int per = (nvec + nslice - 1) / nslice;
+    const int nt = (per + kWave - 1) / kWave * kWave;
+    dim3 grid(B, (nvec + nt - 1) / nt), block(nt);
     if (kind == 0)
         hipLaunchKernelGGL(combine_kernel<0>, grid, block, 0, stream, y, row_of, w, K, H, cap, out);
     else if (kind == 1)
