@@ -8,21 +8,34 @@
 // prefill batch (256 rows on average, a few past 300) fits one m-tile, so
 // each weight tile is streamed from HBM once and feeds all of its rows.
 //
-// Operands go from global memory straight into LDS (global_load_lds_dwordx4:
-// each lane's 16 bytes land at the wave's LDS base + 16 * lane) through two
-// k-step buffers.  Each buffer is its own __shared__ object and the k loop is
-// unrolled by two so every LDS access names its buffer statically: the
+// Operands go from global memory straight into LDS by buffer loads
+// (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the wave's LDS
+// base + 16 * lane) through two k-step buffers.  A scalar buffer resource per
+// operand bounds its extent, so rows past the tile's valid rows (and weight
+// rows past N) read no memory and land zeros, and every stage is the same
+// LPS loads per wave.  Each buffer is its own __shared__ object and the k loop
+// is unrolled by two so every LDS access names its buffer statically: the
 // compiler can then see that reads of one stage do not alias the loads in
 // flight into the other and does not drain the loads before every LDS read.
 // The 16-byte chunks of a row are XOR-swizzled by (row & 7) so the 16 rows
-// one MFMA operand read touches fall into distinct LDS banks; the direct
-// loads permute which global chunk each lane fetches to produce that layout.
+// one MFMA operand read touches fall into distinct LDS banks; the loads
+// permute which global chunk each lane fetches to produce that layout.
 //
-// Measured limits on MI355X that shaped this: the kernel is bound by its load
-// pipeline, not by MFMA or LDS bandwidth; deeper direct-load rings (32-wide
-// k-steps in 4 or 5 stages, or a separate weight ring loaded by dedicated
-// waves) did not help, and a wave with a dozen or more strided direct loads
-// outstanding slows down sharply.
+// A wave's valid row fragments are a prefix of its fragments, so the tile
+// runs one of FM + 1 copies of the k loop, selected by that count: no branch
+// inside a step, so the compiler keeps the accumulators in place, prefetches
+// the next fragment's rows under the current fragment's MFMAs, and the next
+// stage's loads go out one after each fragment's MFMA group (the order is
+// pinned with scheduling fences).  Issued all at once, they stalled every
+// wave of the workgroup on a full memory queue for 800-1400 cycles per step.
+//
+// Measured limits on MI355X that shaped this: per k-step the loads of the
+// next stage (32 KB of weights from HBM, 32-40 KB of rows from L2) take about
+// as long as the MFMA work of the current one, and the two waves that share a
+// SIMD finish their MFMA groups about 1000 cycles apart.  Issuing the next
+// stage before waiting for the current one (two stages in flight, with a
+// second barrier per step), loads in the order weights first, and two loads
+// per fragment were each measured slower; deeper rings do not fit in LDS.
 #pragma once
 
 #include <type_traits>
@@ -73,6 +86,25 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
 }
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
+
+// Buffer resource over [base, base + bytes): raw (stride 0), so an access
+// at byte offset o >= bytes is out of range: it reads no memory and returns
+// zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;      // 32-bit data format, no swizzle
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// 16 bytes per lane through a buffer resource straight into LDS at
+// lds_wave_base + 16 * lane (the device-pass-only wrapper of lds_dma16).
+template <int CPOL>
+__device__ __forceinline__ void lds_buf16(rsrc_t r, void* lds_wave_base, uint32_t voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                             (int)voff, soff, 0, CPOL);
+#endif
+}
 
 // 8 waves laid out 2 (rows) x 4 (weight rows).  A wave owns the interleaved
 // 16-row fragments {wm, wm + 2, ...} (so a short tile still spreads its valid
@@ -137,60 +169,57 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
         const uint16_t* wg = W0 + (size_t)j * N * Kdim;
         const uint16_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
 
-        // per-lane source offsets of this wave's direct loads (fixed for the tile),
-        // 32-bit, relative to the row tensor or to the expert's weight matrices;
-        // lanes past the valid rows / columns re-read row 0 so every stage is
-        // exactly LPS vector-memory instructions per wave
+        // Operands come in by buffer loads straight into LDS: a scalar resource
+        // per operand (base, byte extent) plus a 32-bit per-lane offset and the
+        // k-step as scalar offset.  Rows past the tile's valid rows and weight
+        // rows past N lie outside their resource's extent, so those lanes read
+        // nothing from memory and land zeros.  Each lane's offset is fixed for
+        // the tile.
         const char* abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
-        const char* gbase = reinterpret_cast<const char*>(wg);
-        const char* ubase = reinterpret_cast<const char*>(wu);
+        const uint32_t a_bytes = (uint32_t)nvalid * (uint32_t)(Kdim * 2);
+        const uint32_t w_bytes = (uint32_t)N * (uint32_t)(Kdim * 2);
         uint32_t off[LPS];
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
             const bool is_a = i < A_ITERS;
             const int r = (is_a ? i * NW : (i - A_ITERS) * NW) * 8 + wave * 8 + lane / 8;
             const uint32_t c16 = (uint32_t)swz(r, lane % 8) * 16;   // logical chunk this lane fetches
-            if (is_a) {
-                off[i] = (uint32_t)(r < nvalid ? r : 0) * (uint32_t)(Kdim * 2) + c16;
-            } else {
-                const int rr = (GATED && r >= BN / 2) ? r - BN / 2 : r;
-                const int col = col0 + rr;
-                off[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)(Kdim * 2) + c16;
-            }
+            const int rr = (!is_a && GATED && r >= BN / 2) ? r - BN / 2 : r;
+            off[i] = (uint32_t)(is_a ? r : col0 + rr) * (uint32_t)(Kdim * 2) + c16;
         }
-        auto issue = [&](auto I, int kstep) {
-#pragma unroll
-            for (int i = 0; i < LPS; ++i) {
-                const bool is_a = i < A_ITERS;
-                const bool up = GATED && i >= A_ITERS + G_ITERS;
-                const char* b = is_a ? abase : (up ? ubase : gbase);
-                char* dst = is_a ? a_base(I) + (i * NW + wave) * 1024
-                                 : b_base(I) + ((i - A_ITERS) * NW + wave) * 1024;
-                // weight tiles are read by one or two m-tiles of an expert, all
-                // close together in tile order; the row block is re-read by
-                // every n-tile, so only the weights stream.  Row blocks wholly
-                // past the valid rows are not loaded (wave-uniform): their
-                // stale LDS rows feed only outputs that are never stored.
-                if (is_a) {
-                    if ((i * NW + wave) * 8 < nvalid) lds_dma16<0>(b + off[i] + (size_t)kstep * BK * 2, dst);
-                } else
-                    lds_dma16<kNonTemporal>(b + off[i] + (size_t)kstep * BK * 2, dst);
-            }
+        // direct load i of a stage; `live` false (the step after the last) reads
+        // nothing, so every step issues the same LPS loads without a branch
+        auto issue_one = [&](auto I, int i, int kstep, bool live) {
+            const bool is_a = i < A_ITERS;
+            const bool up = GATED && i >= A_ITERS + G_ITERS;
+            char* dst = is_a ? a_base(I) + (i * NW + wave) * 1024
+                             : b_base(I) + ((i - A_ITERS) * NW + wave) * 1024;
+            // the step after the last gets an empty extent: every access out of range
+            const rsrc_t r = make_rsrc(is_a ? (const void*)abase : (up ? (const void*)wu : (const void*)wg),
+                                       live ? (is_a ? a_bytes : w_bytes) : 0u);
+            // the row block is re-read by every n-tile of the expert (kept in
+            // L2); weight tiles are read by one or two m-tiles close together in
+            // tile order, so only the weights stream (non-temporal)
+            if (is_a)
+                lds_buf16<0>(r, dst, off[i], kstep * BK * 2);
+            else
+                lds_buf16<kNonTemporal>(r, dst, off[i], kstep * BK * 2);
         };
 
-        floatx4 acc[FM][FN];
+        // per-lane LDS byte offset of the 16-byte chunk this lane feeds to an
+        // MFMA at half-step kk, for any operand row that is a multiple of 16
+        // plus (lane & 15): the swizzle then depends on the lane alone
+        int lds_lane[2];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int f = 0; f < FN; ++f) acc[i][f] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-        auto brow = [&](int f) {      // B-tile row of this lane for n-fragment f
+        for (int kk = 0; kk < 2; ++kk)
+            lds_lane[kk] = (lane & 15) * ROWB + (((kk * 4 + (lane >> 4)) ^ (lane & 7)) * 16);
+        auto brow0 = [&](int f) {     // first B-tile row of n-fragment f
             if (GATED) {
                 const int half = f < FN / 2 ? 0 : BN / 2;
                 const int ff = f < FN / 2 ? f : f - FN / 2;
-                return half + wn * (WN / 2) + ff * 16 + (lane & 15);
+                return half + wn * (WN / 2) + ff * 16;
             }
-            return wn * WN + f * 16 + (lane & 15);
+            return wn * WN + f * 16;
         };
         auto fcol = [&](int f) {      // output column of fragment f's first lane column
             if (GATED) {
@@ -200,74 +229,122 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
             return col0 + wn * WN + f * 16;
         };
 
-        // v_mfma_f32_16x16x32_bf16: lane l feeds row (l % 16) with k-chunk (l / 16)
-        // of the 32-wide step for both operands and receives rows 4*(l/16)+e,
-        // column l % 16 of the 16x16 result
-        auto compute = [&](auto I) {
-            const char* ab = a_base(I);
-            const char* bb = b_base(I);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int c = kk * 4 + (lane >> 4);
-                bf16x8 bfr[FN];
-#pragma unroll
-                for (int f = 0; f < FN; ++f) {
-                    const int r = brow(f);
-                    bfr[f] = *reinterpret_cast<const bf16x8*>(bb + r * ROWB + swz(r, c) * 16);
-                }
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    const int mrow = (wm + WMW * i) * 16;
-                    if (mrow < nvalid) {
-                        const int r = mrow + (lane & 15);
-                        const bf16x8 afr = *reinterpret_cast<const bf16x8*>(ab + r * ROWB + swz(r, c) * 16);
-#pragma unroll
-                        for (int f = 0; f < FN; ++f)
-                            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[f], acc[i][f], 0, 0, 0);
-                    }
-                }
-            }
-        };
+        // this wave's valid 16-row fragments are i < nf (rows (wm + 2 i) * 16 ...)
+        const int nf = __builtin_amdgcn_readfirstlane(
+            nvalid > wm * 16 ? min(FM, (nvalid - wm * 16 + 31) / 32) : 0);
 
         // the previous tile's reads of both stages must be complete before new loads land
         wait_lgkm0();
         block_barrier();
-        issue(ic<0>{}, 0);
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) issue_one(ic<0>{}, i, 0, true);
 
-        // step k: wait for stage k (nothing else is in flight), then load k+1
-        // into the other buffer while computing k
-        auto step = [&](auto I, int k) {
-            constexpr int s = decltype(I)::value;
+        // The tile for NF valid fragments: no branch inside a step.
+        // v_mfma_f32_16x16x32_bf16: lane l feeds row (l % 16) with k-chunk (l / 16)
+        // of the 32-wide step for both operands and receives rows 4*(l/16)+e,
+        // column l % 16 of the 16x16 result.
+        auto tile = [&](auto NFc) {
+            constexpr int NF = decltype(NFc)::value;
+            floatx4 acc[NF > 0 ? NF : 1][FN];
+#pragma unroll
+            for (int i = 0; i < NF; ++i)
+#pragma unroll
+                for (int f = 0; f < FN; ++f) acc[i][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+            // compute stage I while issuing the next stage's LPS loads, one
+            // after each fragment's MFMA group (the rest, if there are fewer
+            // groups than loads, at the end), so the waves do not all stall at
+            // once on a full memory queue
+            auto compute = [&](auto I, int knext, bool live) {
+                const char* ab = a_base(I);
+                const char* bb = b_base(I);
+                constexpr auto nextbuf = ic<1 - decltype(I)::value>{};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 bfr[FN];
+#pragma unroll
+                    for (int f = 0; f < FN; ++f)
+                        bfr[f] = *reinterpret_cast<const bf16x8*>(bb + lds_lane[kk] + brow0(f) * ROWB);
+                    bf16x8 acur;
+                    if (NF > 0) acur = *reinterpret_cast<const bf16x8*>(ab + lds_lane[kk] + wm * 16 * ROWB);
+#pragma unroll
+                    for (int i = 0; i < NF; ++i) {
+                        bf16x8 anext;      // next fragment's rows, read under this one's MFMAs
+                        if (i + 1 < NF)
+                            anext = *reinterpret_cast<const bf16x8*>(
+                                ab + lds_lane[kk] + (wm + WMW * (i + 1)) * 16 * ROWB);
+#pragma unroll
+                        for (int f = 0; f < FN; ++f)
+                            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur, bfr[f], acc[i][f], 0, 0, 0);
+                        const int slot = kk * NF + i;
+                        if (slot < LPS) issue_one(nextbuf, slot, knext, live);
+                        if (i + 1 < NF) acur = anext;
+                        // keep this order: the loads go out one per fragment, early
+                        // in the step, between MFMA groups
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                if (2 * NF < LPS) {
+#pragma unroll
+                    for (int q = 2 * NF; q < LPS; ++q) issue_one(nextbuf, q, knext, live);
+                }
+            };
+
+            // step k: wait for stage k (nothing else is in flight), then compute
+            // k while stage k + 1 is loaded into the other buffer
+            auto step = [&](auto I, int k) {
+                wait_vmcnt<0>();
+                wait_lgkm0();
+                block_barrier();
+                // wave-uniform by construction; say so, so that the resource
+                // select below stays scalar
+                const bool live = __builtin_amdgcn_readfirstlane(k + 1 < nk ? 1 : 0) != 0;
+                compute(I, k + 1, live);
+            };
+            for (int k = 0; k < nk; k += 2) {
+                step(ic<0>{}, k);
+                if (k + 1 < nk) step(ic<1>{}, k + 1);
+            }
+            // the loads issued by the last step read nothing but still count
             wait_vmcnt<0>();
-            wait_lgkm0();
-            block_barrier();
-            if (k + 1 < nk) issue(ic<1 - s>{}, k + 1);
-            compute(I);
-        };
-        for (int k = 0; k < nk; k += 2) {
-            step(ic<0>{}, k);
-            if (k + 1 < nk) step(ic<1>{}, k + 1);
-        }
 
-        // ---- epilogue
-        constexpr int FO = GATED ? FN / 2 : FN;
+            // ---- epilogue
+            constexpr int FO = GATED ? FN / 2 : FN;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int mrow = (wm + WMW * i) * 16;
-            if (mrow >= nvalid) continue;
+            for (int i = 0; i < NF; ++i) {
+                const int mrow = (wm + WMW * i) * 16;
 #pragma unroll
-            for (int f = 0; f < FO; ++f) {
-                const int col = fcol(f) + (lane & 15);
-                if (col >= N) continue;
+                for (int f = 0; f < FO; ++f) {
+                    const int col = fcol(f) + (lane & 15);
+                    if (col >= N) continue;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = mrow + (lane >> 4) * 4 + e;
-                    if (r < nvalid) {
-                        const float val = GATED ? silu(acc[i][f][e]) * acc[i][f + FN / 2][e] : acc[i][f][e];
-                        Out[(size_t)(row0 + r) * N + col] = (uint16_t)f32_to_bf16_bits(val);
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = mrow + (lane >> 4) * 4 + e;
+                        if (r < nvalid) {
+                            const float val = GATED ? silu(acc[i][f][e]) * acc[i][f + FN / 2][e] : acc[i][f][e];
+                            Out[(size_t)(row0 + r) * N + col] = (uint16_t)f32_to_bf16_bits(val);
+                        }
                     }
                 }
             }
+        };
+        // a switch, not a chain of ifs: with the chain the compiler no longer
+        // treated the tile's scalars as uniform and wrapped every buffer load
+        // in a readfirstlane loop
+        static_assert(FM <= 10, "one case per fragment count");
+        switch (nf) {
+            case 0: if constexpr (0 <= FM) tile(ic<0>{}); break;
+            case 1: if constexpr (1 <= FM) tile(ic<1>{}); break;
+            case 2: if constexpr (2 <= FM) tile(ic<2>{}); break;
+            case 3: if constexpr (3 <= FM) tile(ic<3>{}); break;
+            case 4: if constexpr (4 <= FM) tile(ic<4>{}); break;
+            case 5: if constexpr (5 <= FM) tile(ic<5>{}); break;
+            case 6: if constexpr (6 <= FM) tile(ic<6>{}); break;
+            case 7: if constexpr (7 <= FM) tile(ic<7>{}); break;
+            case 8: if constexpr (8 <= FM) tile(ic<8>{}); break;
+            case 9: if constexpr (9 <= FM) tile(ic<9>{}); break;
+            case 10: if constexpr (10 <= FM) tile(ic<10>{}); break;
+            default: break;
         }
     }
 }

@@ -8,7 +8,8 @@ scales); y on the valid rows and out meet the layer's tolerance.
 Graph replay: the six calls of one layer step captured once and replayed;
 every replay (after clearing the outputs, with eager steps and host
 synchronisations in between) must reproduce the eager result bit for bit,
-since every kernel is deterministic.
+since every kernel is deterministic, and each replay's output is also
+checked against the oracle's layer (row_of exact, out within tolerance).
 """
 import gc
 
@@ -124,6 +125,14 @@ def test_graph_replay_matches_eager(cfg, layout):
             layer.forward(case.x_dev, case.logits_dev, case.wdict)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
+    # the eager result itself against the oracle (layout exact, out within tolerance)
+    c = case.cfg
+    if layout == "masked":
+        o = _oracle_masked(case, layer.cap_e)
+    else:
+        o = case.oracle_layer()
+    np.testing.assert_array_equal(ref_row_of.cpu().numpy(), o["row_of"])
+    assert_close(to_np(ref_out), o["out"], c.act_dtype, "out (eager, before capture)")
     for rep in range(3):
         layer.out.zero_()
         layer.row_of.fill_(-7)
@@ -132,6 +141,7 @@ def test_graph_replay_matches_eager(cfg, layout):
         torch.cuda.synchronize()
         assert torch.equal(layer.out, ref_out), f"replay {rep}: out differs from the eager result"
         assert torch.equal(layer.row_of, ref_row_of), f"replay {rep}: row_of differs"
+        assert_close(to_np(layer.out), o["out"], c.act_dtype, f"out (replay {rep}) against the oracle")
         layer.forward(case.x_dev, case.logits_dev, case.wdict)   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(layer.out, ref_out)

@@ -69,7 +69,8 @@ MB = [
 @pytest.mark.parametrize("cfg", MB, ids=[c.name for c in MB])
 def test_two_micro_batches_match_single_batch(cfg):
     """Two micro-batches on two streams give the single-batch layer's output
-    bit for bit (Moreh report, compute-communication overlapping)."""
+    bit for bit (Moreh report, compute-communication overlapping), and that
+    output matches the oracle's layer."""
     from combine_grouped_gemm_amd import MoELayer
     from combine_grouped_gemm_amd.layer import MicroBatchedLayer
     print(f"[micro-batches] {cfg.name} T={cfg.T}", flush=True)
@@ -85,6 +86,28 @@ def test_two_micro_batches_match_single_batch(cfg):
         oa, ob = two.forward(x, logits, w)
         torch.cuda.synchronize()
         assert torch.equal(torch.cat([oa, ob]), ref)
+    # and against the oracle: each micro-batch routes and lays out its own tokens
+    # exactly as the oracle does for them, and the joined output meets the layer's
+    # tolerance against the oracle's whole-batch layer
+    x_np = np.concatenate([to_np(s) for s in wl.gen_x(cfg)])
+    lg_np = wl.gen_logits(cfg).numpy()
+
+    def weights_of(j):
+        d = W.expert(j, "cpu")
+        return tuple(to_np(d[k]) for k in ("gate", "up", "down"))
+
+    o = oracle.layer(x_np, lg_np, cfg.K, cfg.E, cfg.e_begin, cfg.e_end, weights_of, cfg.act_dtype,
+                     cfg.y_dtype, cfg.out_dtype)
+    Ta = two.a.T
+    for part, rows in ((two.a, slice(0, Ta)), (two.b, slice(Ta, cfg.T))):
+        ids_p, _ = oracle.route(lg_np[rows], cfg.K)
+        lay_p = oracle.layout(ids_p, cfg.E, cfg.e_begin, cfg.e_end, part.cap)
+        np.testing.assert_array_equal(part.topk_ids.cpu().numpy(), ids_p)
+        np.testing.assert_array_equal(part.row_of.cpu().numpy(), lay_p["row_of"])
+        np.testing.assert_array_equal(part.offsets.cpu().numpy(), lay_p["offsets"])
+    np.testing.assert_array_equal(np.concatenate([two.a.topk_ids.cpu().numpy(),
+                                                  two.b.topk_ids.cpu().numpy()]), o["ids"])
+    assert_close(to_np(torch.cat([oa, ob])), o["out"], cfg.act_dtype, "out (two micro-batches)")
     del one, two, W
     gc.collect()
     torch.cuda.empty_cache()

@@ -123,3 +123,32 @@ def test_ep8_share_routing_imbalance_drops_to_within_5_percent():
     assert eplb.balance_stats(eplb.group_loads(load1, phys, G))["max_over_min"] < 1.15
     # the remapped routing routes every slot to the physical id of its expert
     np.testing.assert_array_equal(eplb.remap_ids(ids, phys), np.asarray(phys)[ids])
+
+
+def test_balance_stats_hand_computed():
+    """Per-group loads [3, 1, 2] by hand: max/min = 3/1 = 3, mean = 2 so
+    max/mean = 3/2 = 1.5, and SGLang's balancedness mean/max = 2/3.  The three
+    figures differ from each other, so an exchanged or inverted formula fails."""
+    s = eplb.balance_stats([3, 1, 2])
+    assert s["max_over_min"] == 3.0
+    assert s["max_over_mean"] == 1.5
+    assert abs(s["balancedness"] - 2.0 / 3.0) < 1e-15
+    # [4, 1, 1]: max/min 4, mean 2 -> max/mean 2, balancedness 1/2
+    s = eplb.balance_stats([4, 1, 1])
+    assert (s["max_over_min"], s["max_over_mean"], s["balancedness"]) == (4.0, 2.0, 0.5)
+    # a group with no load: max/min is unbounded, the other two stay finite
+    s = eplb.balance_stats([2, 0])
+    assert s["max_over_min"] == float("inf") and s["max_over_mean"] == 2.0 and s["balancedness"] == 0.5
+
+
+def test_remap_ids_hand_worked():
+    """Logical experts 0..3 placed at physical ids [2, 0, 3, 1] (logical 0 sits
+    at physical 2, logical 1 at 0, ...).  Tokens routed to logical [[0, 3],
+    [1, 2]] go to physical [[2, 1], [0, 3]].  Reading the table the other way
+    round (physical -> logical, i.e. its inverse [1, 3, 0, 2]) would give
+    [[1, 2], [3, 0]], so the direction of the map is pinned."""
+    phys = np.array([2, 0, 3, 1], dtype=np.int32)
+    got = eplb.remap_ids(np.array([[0, 3], [1, 2]]), phys)
+    assert got.dtype == np.int32
+    assert got.tolist() == [[2, 1], [0, 3]]
+    assert got.tolist() != np.argsort(phys)[np.array([[0, 3], [1, 2]])].tolist()
