@@ -1,17 +1,28 @@
 """Bench of the single-GPU expert-parallel MoE layer on MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-others]
 
 One step is one pass of the whole path -- route, layout, dispatch, gate/up
 GEMM + SwiGLU, down GEMM, combine -- over one batch of seeded synthetic
-input already resident in HBM.  The default workload is the DeepSeek-V3
-shaped decode step (T=128, E=256, K=8, H=7168, I=2048, bf16).  Each stage
-is bracketed by HIP events on the launch stream during the timed steps, so
-per-kernel durations, algorithmic GB/s and TFLOP/s come from the same run.
+input already resident in HBM.  The headline workload is the DeepSeek-V3
+shaped prefill step (T=8192, E=256, K=8, H=7168, I=2048, bf16), the largest
+configuration and the one the grouped-GEMM bar applies to.
 
-Prints one JSON line (rank 0).  A CPU baseline -- the oracle as it stands,
-timed on a bounded sample of the same workload on the host cores -- is
-included unless --no-cpu-baseline is given.
+Timed steps run cold: they rotate over enough independent sets of input and
+activation buffers (x, logits, routing, Xd, h, y, out) that the sets together
+exceed twice the 256 MB Infinity Cache, so no step finds the previous
+step's activations in cache (a producer's output inside one step still may,
+as in a real layer).  The expert weights are shared and far larger than the
+cache.  A second, warm pass repeats the steps on one buffer set and is
+reported beside them.  Each stage is bracketed by HIP events on the launch
+stream, so per-kernel durations, algorithmic GB/s and TFLOP/s come from the
+same run.
+
+Prints one JSON line (rank 0).  The other workloads (toy, decode, EP-share,
+GPT-OSS) are timed the same way after the headline and reported as
+sub-objects of that line unless --no-others is given.  A CPU baseline --
+the oracle as it stands, timed on a bounded sample of the headline workload
+on the host cores -- is included unless --no-cpu-baseline is given.
 """
 from __future__ import annotations
 
@@ -40,7 +51,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3_decode", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--workload", default="dsv3_prefill", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--no-others", action="store_true",
+                    help="time only --workload (no sub-objects for the other workloads)")
+    ap.add_argument("--cold-mb", type=int, default=512,
+                    help="rotate buffer sets until they exceed this many MB (0: one set, warm only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="target CPU seconds for the oracle sample")
@@ -288,11 +303,228 @@ def cpu_baseline(cfg, x_cpu, logits_cpu, weights, budget_s):
     oracle.combine(y, lay["row_of"], gates, cfg.out_dtype)
     t_comb = time.perf_counter() - t4
     est = t_route_layout + (t_disp + t_ffn) * scale + t_comb
+    extrapolated = done < len(touched)
     return {"value": round(cfg.T / est, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "extrapolated": extrapolated,
             "sample": (f"route+layout+combine on all {cfg.T} tokens; dispatch+FFN on {done} of "
-                       f"{len(touched)} touched experts ({rows_done} of {R} rows), scaled by "
-                       f"{scale:.2f}; weight fetch to host untimed"),
-            "measured_s": round(t_route_layout + t_disp + t_ffn + t_comb, 2)}
+                       f"{len(touched)} touched experts ({rows_done} of {R} rows)"
+                       + (f", extrapolated linearly to all touched experts (x{scale:.2f})" if extrapolated
+                          else ", no extrapolation")
+                       + "; weight fetch to host untimed"),
+            "measured_s": round(t_route_layout + t_disp + t_ffn + t_comb, 2),
+            "toy_single_thread": toy_single_thread()}
+
+
+def toy_single_thread(reps=5):
+    """The oracle's whole toy layer (8 x 8 tokens, E=16, K=2, H=128, I=256,
+    fp32) with its numerical libraries held to one thread: tokens/s, best of
+    `reps` runs."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    cfg = wl.CONFIGS["toy"]
+    xs = wl.gen_x(cfg)
+    x = np.concatenate([t.numpy().astype(np.float64) for t in xs])
+    lg = wl.gen_logits(cfg, xs).numpy()
+    W = wl.gen_expert_weights(cfg, "cpu")
+    mats = [tuple(t[j].double().numpy() for t in (W.gate, W.up, W.down)) for j in range(cfg.E_loc)]
+    best = float("inf")
+    with threadpool_limits(limits=1):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.layer(x, lg, cfg.K, cfg.E, cfg.e_begin, cfg.e_end, lambda j: mats[j],
+                         cfg.act_dtype, cfg.y_dtype, cfg.out_dtype)
+            best = min(best, time.perf_counter() - t0)
+    return {"value": round(cfg.T / best, 1), "unit": "tokens/s", "cores": 1, "workload": "toy",
+            "note": "whole toy layer, best of 5, one thread"}
+
+
+def _act_bytes(cfg, R):
+    """Bytes of one buffer set a step touches: inputs, routing and the
+    activations of the R dispatched rows."""
+    sx, sa, sy, so = (ESIZE[cfg.x_dtype], ESIZE[cfg.act_dtype], ESIZE[cfg.y_dtype], ESIZE[cfg.out_dtype])
+    return cfg.T * cfg.H * (sx + so) + cfg.T * cfg.E * 4 + R * (cfg.H * sa + cfg.I * sa + cfg.H * sy)
+
+
+def _time_steps(sets, stages_of, steps, warmup, stream):
+    """warmup + steps steps, step s on buffer set s % len(sets); returns
+    (wall ms per step, per-stage event ms lists, per-step event ms)."""
+    nset = len(sets)
+    for s in range(warmup):
+        for _, run in stages_of[s % nset]:
+            run()
+    torch.cuda.synchronize()
+    n_st = len(stages_of[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, (_, run) in enumerate(stages_of[s % nset]):
+            run()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = [n for n, _ in stages_of[0]]
+    per = {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i, n in enumerate(names)}
+    step_ms = [ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]
+    return wall * 1e3 / steps, per, step_ms
+
+
+def _stage_report(per, work, mfma_peak, copy_gbs):
+    rep = {}
+    for name, times in per.items():
+        ms = float(np.mean(times))
+        t = ms / 1e3
+        r = roofline_of(work[name], ms, mfma_peak)
+        rep[name] = {"ms": round(ms, 4), "ms_median": round(float(np.median(times)), 4),
+                     "ms_p10": round(float(np.percentile(times, 10)), 4),
+                     "ms_p90": round(float(np.percentile(times, 90)), 4),
+                     "GB_s": round(work[name]["bytes"] / t / 1e9, 1),
+                     "TFLOP_s": round(work[name]["flops"] / t / 1e12, 2),
+                     "hbm_frac": round(work[name]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_frac": round(work[name]["flops"] / t / 1e12 / mfma_peak, 4),
+                     "copy_frac": round(work[name]["bytes"] / t / 1e9 / copy_gbs, 4),
+                     "bytes": int(work[name]["bytes"]), "flops": int(work[name]["flops"]),
+                     "bound": r["bound"]}
+    return rep
+
+
+def run_workload(m, cfg, a, dev, copy_gbs, headline):
+    """Time one workload; returns its report (the full line for the headline,
+    a compact object otherwise)."""
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    x_cpu = wl.gen_x(cfg)
+    logits_cpu = wl.gen_logits(cfg, x_cpu)
+    placement = None
+    if headline and a.eplb:
+        placement = eplb_placement(m, cfg, dev)
+        W = wl.gen_expert_weights(cfg, device=dev, experts=placement["local_logical"])
+    elif headline and a.shared_experts:
+        if cfg.e_end != cfg.E:
+            raise SystemExit("--shared-experts needs the local range to end at E")
+        W = wl.gen_expert_weights(cfg, device=dev,
+                                  experts=list(range(cfg.e_begin, cfg.E + a.shared_experts)))
+    else:
+        W = wl.gen_expert_weights(cfg, device=dev)
+    wdict = W.as_dict()
+    layout = a.layout if headline else "contiguous"
+    n_shared = a.shared_experts if headline else 0
+
+    def new_layer():
+        L = m.MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end,
+                       cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=dev, layout=layout,
+                       cap_per_expert=(a.cap_per_expert or None) if headline else None,
+                       n_shared=n_shared)
+        if placement is not None:
+            L.expert_map = placement["map"]
+        return L
+
+    layer = new_layer()
+    x = [t.to(dev) for t in x_cpu]
+    logits = logits_cpu.to(dev)
+
+    # parity gate before timing: routing and layout must equal the oracle's
+    layer.forward(x, logits, wdict)
+    torch.cuda.synchronize()
+    import oracle
+    if n_shared:
+        ids, _ = oracle.route_shared(logits_cpu.numpy(), cfg.K, n_shared)
+    else:
+        ids, _ = oracle.route(logits_cpu.numpy(), cfg.K)
+    if placement is not None:
+        ids = placement["phys"][ids]
+    lay = oracle.layout(ids, layer.E, layer.e_begin, layer.e_end, layer.cap)
+    ref_row_of = (oracle.layout_masked(ids, cfg.E, cfg.e_begin, cfg.e_end, layer.cap_e)["row_of"]
+                  if layer.masked else lay["row_of"])
+    if not (np.array_equal(layer.topk_ids.cpu().numpy(), ids)
+            and np.array_equal(layer.row_of.cpu().numpy(), ref_row_of)):
+        raise RuntimeError(f"parity gate failed on {cfg.name}: routing/layout differ from the oracle")
+    counts_local = lay["counts"][layer.e_begin:layer.e_end]
+    local = (ids >= layer.e_begin) & (ids < layer.e_end)
+    work, R, touched = stage_work(cfg, counts_local, int(local.any(axis=1).sum()), layer.K)
+
+    # buffer sets for the cold pass: the same inputs copied into independent
+    # buffers (the copies give identical routing, so the algorithmic work is
+    # the same on every set)
+    per_set = _act_bytes(cfg, R)
+    n_sets = 1 if a.cold_mb <= 0 else max(2, min(16, int(a.cold_mb * 2**20 // max(per_set, 1)) + 1))
+    sets = [(layer, x, logits)]
+    for _ in range(n_sets - 1):
+        sets.append((new_layer(), [t.clone() for t in x], logits.clone()))
+    stages_of = [L.stages(xs, lg, wdict) for (L, xs, lg) in sets]
+    stream = torch.cuda.current_stream()
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.act_dtype]
+
+    print(f"[bench] {cfg.name}: timing {a.steps} cold steps over {n_sets} buffer sets",
+          file=sys.stderr, flush=True)
+    ms_cold, per_cold, step_cold = _time_steps(sets, stages_of, a.steps, a.warmup, stream)
+    print(f"[bench] {cfg.name}: timing {a.steps} warm steps on one buffer set", file=sys.stderr, flush=True)
+    ms_warm, per_warm, step_warm = _time_steps(sets[:1], stages_of[:1], a.steps, a.warmup, stream)
+    cold = _stage_report(per_cold, work, mfma_peak, copy_gbs)
+    warm = _stage_report(per_warm, work, mfma_peak, copy_gbs)
+    dom = max(cold, key=lambda k: cold[k]["ms"])
+    roof = roofline_of(work[dom], cold[dom]["ms"], mfma_peak)
+    traffic = measured_traffic(cfg.name)
+    roof.update({"kernel": dom, "traffic": (int(traffic[dom]) if traffic and dom in traffic else None),
+                 "algorithmic_bytes": int(work[dom]["bytes"]), "algorithmic_flops": int(work[dom]["flops"]),
+                 "hbm_frac": cold[dom]["hbm_frac"], "mfma_frac": cold[dom]["mfma_frac"]})
+    ffn_ms = cold["ffn_gate_up"]["ms"] + cold["ffn_down"]["ms"]
+    ffn_flops = work["ffn_gate_up"]["flops"] + work["ffn_down"]["flops"]
+    ffn_bytes = work["ffn_gate_up"]["bytes"] + work["ffn_down"]["bytes"]
+    grouped = {"ms": round(ffn_ms, 4), "TFLOP_s": round(ffn_flops / (ffn_ms / 1e3) / 1e12, 2),
+               "mfma_frac": round(ffn_flops / (ffn_ms / 1e3) / 1e12 / mfma_peak, 4),
+               "GB_s": round(ffn_bytes / (ffn_ms / 1e3) / 1e9, 1),
+               "hbm_frac": round(ffn_bytes / (ffn_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    warm_brief = {"ms_per_step": round(ms_warm, 4),
+                  "tokens_per_s": round(cfg.T / (ms_warm / 1e3), 1),
+                  "stages": {k: {"ms": v["ms"], "GB_s": v["GB_s"], "hbm_frac": v["hbm_frac"]}
+                             for k, v in warm.items()}}
+    config = {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "K": cfg.K, "H": cfg.H, "I": cfg.I,
+              "local_experts": [cfg.e_begin, cfg.e_end], "segments": len(cfg.seg_rows),
+              "rows": R, "experts_touched": touched,
+              "buffer_sets": n_sets, "buffer_set_MB": round(per_set / 2**20, 1),
+              **({"weight_scales": cfg.w_scales} if cfg.w_dtype == "fp8" else {})}
+    if not headline:
+        out = {"value": round(cfg.T / (ms_cold / 1e3), 1), "unit": "tokens/s",
+               "ms_per_step": round(ms_cold, 4), "dtype": cfg.act_dtype, "config": config,
+               "roofline": roof, "grouped_ffn": grouped,
+               "stages": {k: {"ms": v["ms"], "GB_s": v["GB_s"], "TFLOP_s": v["TFLOP_s"],
+                              "hbm_frac": v["hbm_frac"], "mfma_frac": v["mfma_frac"]}
+                          for k, v in cold.items()},
+               "warm": warm_brief}
+        return out, None
+    res = {
+        "metric": "MoE-layer tokens/s on 1 GPU",
+        "value": round(cfg.T / (ms_cold / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_cold, 4),
+        "ms_per_step_events": round(float(np.mean(step_cold)), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.act_dtype, "data": "synthetic (seeded; random-init expert weights)",
+        "config": config,
+        "roofline": roof,
+        "grouped_ffn": grouped,
+        "stages": cold,
+        "warm": warm_brief,
+        "hbm_reference": {"copy_GB_s": round(copy_gbs, 1),
+                          "note": "device-to-device copy of 1 GiB measured in this run (read + write bytes); "
+                                  "copy_frac of a stage = its algorithmic GB/s / this"},
+    }
+    if layout == "masked":
+        res["config"]["layout"] = {"kind": "masked", "cap_per_expert": layer.cap_e}
+    if n_shared:
+        res["config"]["shared_experts"] = n_shared
+    if placement is not None:
+        res["config"]["placement"] = "balanced (8 calibration batches)"
+        res["eplb"] = eplb_report(m, cfg, logits, placement, layer)
+    if a.graph:
+        res["graph_replay"] = graph_replay(layer, x, logits, wdict, a.steps, a.warmup)
+    if a.micro_batches == 2:
+        res["two_micro_batches"] = two_micro_batches(m, cfg, x, logits, wdict, layer, a.steps, a.warmup)
+    keep = (x_cpu, logits_cpu, W)
+    del sets, stages_of
+    return res, keep
 
 
 def main():
@@ -310,132 +542,12 @@ def main():
         cfg = dataclasses.replace(cfg, w_scales=a.w_scales)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
-    x_cpu = wl.gen_x(cfg)
-    logits_cpu = wl.gen_logits(cfg, x_cpu)
-    x = [s.to(dev) for s in x_cpu]
-    logits = logits_cpu.to(dev)
-    placement = None
-    if a.eplb:
-        placement = eplb_placement(m, cfg, dev)
-        W = wl.gen_expert_weights(cfg, device=dev, experts=placement["local_logical"])
-    elif a.shared_experts:
-        if cfg.e_end != cfg.E:
-            raise SystemExit("--shared-experts needs the local range to end at E")
-        W = wl.gen_expert_weights(cfg, device=dev,
-                                  experts=list(range(cfg.e_begin, cfg.E + a.shared_experts)))
-    else:
-        W = wl.gen_expert_weights(cfg, device=dev)
-    wdict = W.as_dict()
-    layer = m.MoELayer(cfg.seg_rows, cfg.E, cfg.K, cfg.H, cfg.I, cfg.e_begin, cfg.e_end,
-                       cfg.act_dtype, cfg.y_dtype, cfg.out_dtype, device=dev, layout=a.layout,
-                       cap_per_expert=(a.cap_per_expert or None), n_shared=a.shared_experts)
-    if placement is not None:
-        layer.expert_map = placement["map"]
-    stages = layer.stages(x, logits, wdict)
-
-    # parity gate before timing: routing and layout must equal the oracle's
-    layer.forward(x, logits, wdict)
-    torch.cuda.synchronize()
-    import oracle
-    if a.shared_experts:
-        ids, _ = oracle.route_shared(logits_cpu.numpy(), cfg.K, a.shared_experts)
-    else:
-        ids, _ = oracle.route(logits_cpu.numpy(), cfg.K)
-    if placement is not None:
-        ids = placement["phys"][ids]
-    lay = oracle.layout(ids, layer.E, layer.e_begin, layer.e_end, layer.cap)
-    ref_row_of = (oracle.layout_masked(ids, cfg.E, cfg.e_begin, cfg.e_end, layer.cap_e)["row_of"]
-                  if layer.masked else lay["row_of"])
-    if not (np.array_equal(layer.topk_ids.cpu().numpy(), ids)
-            and np.array_equal(layer.row_of.cpu().numpy(), ref_row_of)):
-        print(json.dumps({"error": "parity gate failed: routing/layout differ from the oracle"}))
-        sys.exit(1)
-    counts_local = lay["counts"][layer.e_begin:layer.e_end]
-    local = (ids >= layer.e_begin) & (ids < layer.e_end)
-    work, R, touched = stage_work(cfg, counts_local, int(local.any(axis=1).sum()), layer.K)
-
     copy_gbs = measured_copy_gbs(dev)
-    stream = torch.cuda.current_stream()
-    for _ in range(a.warmup):
-        for _, run in stages:
-            run()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({a.warmup} steps), timing {a.steps}", file=sys.stderr, flush=True)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(a.steps):
-        ev[s][0].record(stream)
-        for i, (_, run) in enumerate(stages):
-            run()
-            ev[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {name: [] for name, _ in stages}
-    step_ms = []
-    for s in range(a.steps):
-        for i, (name, _) in enumerate(stages):
-            per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
-        step_ms.append(ev[s][0].elapsed_time(ev[s][-1]))
-    ms_per_step = wall * 1e3 / a.steps
-    mfma_peak = MFMA_PEAK_TFLOPS[cfg.act_dtype]
-    stage_rep = {}
-    for name, _ in stages:
-        ms = float(np.mean(per[name]))
-        r = roofline_of(work[name], ms, mfma_peak)
-        stage_rep[name] = {"ms": round(ms, 4), "ms_median": round(float(np.median(per[name])), 4),
-                           "ms_p10": round(float(np.percentile(per[name], 10)), 4),
-                           "ms_p90": round(float(np.percentile(per[name], 90)), 4),
-                           "GB_s": round(work[name]["bytes"] / (ms / 1e3) / 1e9, 1),
-                           "TFLOP_s": round(work[name]["flops"] / (ms / 1e3) / 1e12, 2),
-                           "hbm_frac": round(work[name]["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "mfma_frac": round(work[name]["flops"] / (ms / 1e3) / 1e12 / mfma_peak, 4),
-                           "copy_frac": round(work[name]["bytes"] / (ms / 1e3) / 1e9 / copy_gbs, 4),
-                           "bytes": int(work[name]["bytes"]), "flops": int(work[name]["flops"]),
-                           "bound": r["bound"]}
-    dom = max(stage_rep, key=lambda k: stage_rep[k]["ms"])
-    roof = roofline_of(work[dom], stage_rep[dom]["ms"], mfma_peak)
-    traffic = measured_traffic(cfg.name)
-    roof.update({"kernel": dom, "traffic": (int(traffic[dom]) if traffic and dom in traffic else None),
-                 "algorithmic_bytes": int(work[dom]["bytes"]), "algorithmic_flops": int(work[dom]["flops"])})
-    ffn_ms = stage_rep["ffn_gate_up"]["ms"] + stage_rep["ffn_down"]["ms"]
-    ffn_flops = work["ffn_gate_up"]["flops"] + work["ffn_down"]["flops"]
-    ffn_bytes = work["ffn_gate_up"]["bytes"] + work["ffn_down"]["bytes"]
-    res = {
-        "metric": "MoE-layer tokens/s on 1 GPU",
-        "value": round(cfg.T / (ms_per_step / 1e3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_events": round(float(np.mean(step_ms)), 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg.act_dtype, "data": "synthetic (seeded; random-init expert weights)",
-        "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "K": cfg.K, "H": cfg.H, "I": cfg.I,
-                   "local_experts": [cfg.e_begin, cfg.e_end], "segments": len(cfg.seg_rows),
-                   "rows": R, "experts_touched": touched,
-                   **({"weight_scales": cfg.w_scales} if cfg.w_dtype == "fp8" else {})},
-        "roofline": roof,
-        "grouped_ffn": {"ms": round(ffn_ms, 4), "TFLOP_s": round(ffn_flops / (ffn_ms / 1e3) / 1e12, 2),
-                        "mfma_frac": round(ffn_flops / (ffn_ms / 1e3) / 1e12 / mfma_peak, 4),
-                        "GB_s": round(ffn_bytes / (ffn_ms / 1e3) / 1e9, 1),
-                        "hbm_frac": round(ffn_bytes / (ffn_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "stages": stage_rep,
-        "hbm_reference": {"copy_GB_s": round(copy_gbs, 1),
-                          "note": "device-to-device copy of 1 GiB measured in this run (read + write bytes); "
-                                  "copy_frac of a stage = its algorithmic GB/s / this"},
-    }
-    if a.layout == "masked":
-        res["config"]["layout"] = {"kind": "masked", "cap_per_expert": layer.cap_e}
-    if a.shared_experts:
-        res["config"]["shared_experts"] = a.shared_experts
-    if placement is not None:
-        res["config"]["placement"] = "balanced (8 calibration batches)"
-        res["eplb"] = eplb_report(m, cfg, logits, placement, layer)
-    if a.graph:
-        res["graph_replay"] = graph_replay(layer, x, logits, wdict, a.steps, a.warmup)
-    if a.micro_batches == 2:
-        res["two_micro_batches"] = two_micro_batches(m, cfg, x, logits, wdict, layer, a.steps, a.warmup)
+    try:
+        res, keep = run_workload(m, cfg, a, dev, copy_gbs, headline=True)
+    except RuntimeError as e:
+        print(json.dumps({"error": str(e)}))
+        sys.exit(1)
     if a.copy_calibration_mib:
         # one elementwise kernel that reads n*4 bytes and writes n*4 bytes
         n = a.copy_calibration_mib * (1 << 20) // 4
@@ -444,9 +556,24 @@ def main():
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
+        del src, dst
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        x_cpu, logits_cpu, W = keep
         res["cpu_baseline"] = cpu_baseline(cfg, x_cpu, logits_cpu, W, a.cpu_budget_s)
+    del keep
+    torch.cuda.empty_cache()
+    if not a.no_others:
+        others = {}
+        for name in ("toy", "dsv3_decode", "ep8_share", "gptoss_fp8", "dsv3_prefill"):
+            if name == cfg.name:
+                continue
+            try:
+                others[name], _ = run_workload(m, wl.CONFIGS[name], a, dev, copy_gbs, headline=False)
+            except Exception as e:  # a failing sub-workload must not hide the headline
+                others[name] = {"error": f"{type(e).__name__}: {e}"}
+            torch.cuda.empty_cache()
+        res["other_workloads"] = others
     print(json.dumps(res), flush=True)
 
 

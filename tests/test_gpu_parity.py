@@ -27,16 +27,16 @@ SMALL = [
     wl.scaled(C["dsv3_prefill"], "prefill_320_row_tiles", seg_rows=(640,), E=4, K=2, H=256, I=192),
     wl.scaled(C["ep8_share"], "ep_small", seg_rows=(100, 37, 64), E=16, K=3, H=256, I=128,
               e_begin=4, e_end=10),
-    wl.scaled(C["gptoss_fp8"], "fp8_small", seg_rows=(300,), E=8, K=2, H=320, I=192),
+    wl.scaled(C["gptoss_fp8"], "fp8_small", seg_rows=(300,), E=8, K=2, H=320, I=192, w_scales="pow2"),
     wl.scaled(C["gptoss_fp8"], "fp8_small_f32_wscales", seg_rows=(300,), E=8, K=2, H=320, I=192,
               w_scales="fp32"),
     wl.scaled(C["gptoss_fp8"], "fp8_wide_f32_wscales", seg_rows=(600,), E=8, K=2, H=640, I=384,
               w_scales="fp32"),
-    wl.scaled(C["gptoss_fp8"], "fp8_decode_real_dims", seg_rows=(24,), E=16, K=4),
+    wl.scaled(C["gptoss_fp8"], "fp8_decode_real_dims", seg_rows=(24,), E=16, K=4, w_scales="pow2"),
     wl.scaled(C["gptoss_fp8"], "fp8_decode_real_dims_f32_wscales", seg_rows=(24,), E=16, K=4, w_scales="fp32"),
     # H = I = 2880: 23 scale blocks per row (whole-row scale runs) and a 64-wide K tail,
     # 48 rows per expert (the wide fp8 tiles), both weight-scale conventions
-    wl.scaled(C["gptoss_fp8"], "fp8_wide_real_dims", seg_rows=(192,), E=8, K=2),
+    wl.scaled(C["gptoss_fp8"], "fp8_wide_real_dims", seg_rows=(192,), E=8, K=2, w_scales="pow2"),
     wl.scaled(C["gptoss_fp8"], "fp8_wide_real_dims_f32_wscales", seg_rows=(200,), E=8, K=2, w_scales="fp32"),
     # fp8 at DeepSeek dimensions: 56 scale blocks per row (past the wide tiles' scale table),
     # ~32 rows per expert through the 128-row fp8 tiles
@@ -45,7 +45,8 @@ SMALL = [
     # kernels' 512 threads, so the largest-first expert ranking and the tile prefix take
     # several passes
     wl.scaled(C["dsv3_prefill"], "prefill_many_experts", seg_rows=(4800,), E=600, K=8, H=128, I=64),
-    wl.scaled(C["gptoss_fp8"], "fp8_wide_many_experts", seg_rows=(3600,), E=600, K=8, H=256, I=128),
+    wl.scaled(C["gptoss_fp8"], "fp8_wide_many_experts", seg_rows=(3600,), E=600, K=8, H=256, I=128,
+              w_scales="pow2"),
     # more than 8 slots per token: combine gathers in passes of 8 slots (two and three passes)
     wl.scaled(C["dsv3_decode"], "decode_k12", seg_rows=(48,), E=32, K=12, H=256, I=128),
     wl.scaled(C["dsv3_prefill"], "prefill_k20", seg_rows=(40,), E=64, K=20, H=128, I=64),
@@ -196,7 +197,8 @@ def test_fp8_pow2_weight_path_matches_generic_path():
     far inside the fp8 tolerance and h codes differ only where a value sits
     on a rounding boundary."""
     from combine_grouped_gemm_amd import moe_ffn_down, moe_ffn_gate_up
-    cfg = wl.scaled(C["gptoss_fp8"], "fp8_po2_vs_generic", seg_rows=(600,), E=8, K=2, H=640, I=384)
+    cfg = wl.scaled(C["gptoss_fp8"], "fp8_po2_vs_generic", seg_rows=(600,), E=8, K=2, H=640, I=384,
+                    w_scales="pow2")
     case = Case(cfg)
     assert case.w.scales_pow2
     layer = run_gpu(case)
@@ -262,10 +264,13 @@ def test_full_size_sampled(name):
     np.testing.assert_array_equal(to_np(layer.xd[torch.as_tensor(rows).cuda()]), ox)
     if cfg.act_dtype == "fp8":
         np.testing.assert_array_equal(layer.xd_scales[torch.as_tensor(rows).cuda()].cpu().numpy(), oxs)
-    # expert outputs: all rows of the busiest local expert and of one random one
+    # expert outputs: all rows of the busiest and of the least busy non-empty local
+    # expert, and of three random ones
     off = lay["offsets"]
-    busiest = int(np.argmax(np.diff(off)))
-    for j in sorted({busiest, int(rng.integers(cfg.E_loc))}):
+    n_rows = np.diff(off)
+    busiest = int(np.argmax(n_rows))
+    quietest = int(np.argmin(np.where(n_rows > 0, n_rows, np.iinfo(np.int64).max)))
+    for j in sorted({busiest, quietest, *(int(v) for v in rng.choice(cfg.E_loc, size=3, replace=False))}):
         a, b = int(off[j]), int(off[j + 1])
         if b == a:
             continue
@@ -274,8 +279,8 @@ def test_full_size_sampled(name):
         xv = oracle.numerics.dequantize_fp8_blocks(xd_o, xs_o) if cfg.act_dtype == "fp8" else xd_o
         y_o = oracle.expert_ffn(xv, *case.oracle_weights(j), cfg.act_dtype, cfg.y_dtype)
         assert_close(to_np(layer.y[a:b]), y_o, cfg.act_dtype, f"y of local expert {j}")
-    # combined rows of three tokens
-    for t in rng.choice(cfg.T, size=3, replace=False):
+    # combined rows of six tokens
+    for t in rng.choice(cfg.T, size=6, replace=False):
         acc = np.zeros(cfg.H)
         xv_t, xs_t = oracle.dispatch(x[t:t + 1], np.zeros((1, 1), np.int64), 1, cfg.act_dtype)
         xv_t = oracle.numerics.dequantize_fp8_blocks(xv_t, xs_t) if cfg.act_dtype == "fp8" else xv_t

@@ -2,10 +2,12 @@
 smoke checks).
 
 This module only draws random inputs; it holds none of the layer's arithmetic
-(no top-K, no grouping, no GEMM, no quantisation rule).  The router projection
-that produces the logits is the layer's input stage and is computed here with
-a plain torch matmul, outside the timed path, so that the oracle and the HIP
-path receive the very same logits tensor.
+(no top-K, no grouping, no GEMM, no activation quantisation).  fp8 expert
+weights are prepared here as an fp8 checkpoint would ship them (codes plus
+block scales, see gen_expert_weights): an input, not a step of the layer.
+The router projection that produces the logits is the layer's input stage
+and is computed here with a plain torch matmul, outside the timed path, so
+that the oracle and the HIP path receive the very same logits tensor.
 
 Workloads (shapes follow the pages: the toy EP layer of "Anatomy of a
 high-performance EP kernel", section "What we have to do"; the 256-expert,
@@ -90,8 +92,8 @@ CONFIGS = {
     "gptoss_fp8": MoEConfig("gptoss_fp8", (4096,), 128, 4, 2880, 2880, 0, 128,
                             "bf16", "fp8", "fp8", "bf16", "bf16", seed=5,
                             description="GPT-OSS-120B-shaped layer, fp8 e4m3 weights and "
-                                        "activations with 1x128 fp32 block scales (powers of two)",
-                            w_scales="pow2"),
+                                        "activations with 1x128 fp32 block scales",
+                            w_scales="fp32"),
 }
 
 
@@ -241,13 +243,15 @@ def gen_expert_weights(cfg: MoEConfig, device="cpu", experts=None) -> ExpertWeig
     weights are the same whichever subset of experts is drawn, but they
     depend on the device's generator (CPU and GPU streams differ).
 
-    fp8 weights are drawn as codes and scales directly: codes ~ e4m3 cast
-    of N(0, 1) * 64 clamped to +-448, and per-block scales
-    s = (1 / (64 * sqrt(fan_in))) * exp(0.1 * N(0, 1)), so code * scale has
-    roughly the N(0, 1/fan_in) spread of the other workloads.  With
-    cfg.w_scales == 'pow2' the scales are powers of two instead,
-    s = 2^(round(log2(1 / (64 * sqrt(fan_in)))) + n) with n = N(0, 1)
-    rounded and clamped to [-2, 2].
+    fp8 weights are fp32 weights ~ N(0, 1/fan_in) stored the way an fp8
+    checkpoint ships them: per output row, one fp32 scale per block of 128
+    input columns (the last block narrower when fan_in is not a multiple of
+    128), s = amax / 448 over the block (1 for an all-zero block), and codes
+    = the e4m3 cast of w / s (torch's conversion, the values clamped to
+    +-448 first).  With cfg.w_scales == 'pow2' each scale is instead the
+    smallest power of two with amax <= 448 * s.  This prepares the inputs
+    only: the layer receives codes and scales, and its own quantisation of
+    activations is defined elsewhere.
     """
     experts = list(range(cfg.e_begin, cfg.e_end)) if experts is None else [int(e) for e in experts]
     E_loc, H, I = len(experts), cfg.H, cfg.I
@@ -269,16 +273,18 @@ def gen_expert_weights(cfg: MoEConfig, device="cpu", experts=None) -> ExpertWeig
         for j, e in enumerate(experts):
             for w, s in enumerate(shapes):
                 g = _expert_generator(cfg, e, w, device)
-                c = (torch.randn(s, generator=g, device=device) * 64.0).clamp_(-448.0, 448.0)
-                codes[w][j].copy_(c.to(torch.float8_e4m3fn))
+                wf = torch.randn(s, generator=g, device=device) / math.sqrt(s[1])
                 nb = scales[w].shape[2]
-                z = torch.randn((s[0], nb), generator=g, device=device)
+                pad = nb * FP8_BLOCK - s[1]
+                amax = torch.nn.functional.pad(wf.abs(), (0, pad)).view(s[0], nb, FP8_BLOCK).amax(dim=2)
+                sc = amax / 448.0
                 if cfg.w_scales == "pow2":
-                    e0 = round(math.log2(1.0 / (64.0 * math.sqrt(s[1]))))
-                    n = torch.round(z).clamp_(-2.0, 2.0).to(torch.int32)
-                    scales[w][j].copy_(((n + (e0 + 127)) << 23).view(torch.float32))   # exact 2^(e0+n)
-                else:
-                    scales[w][j].copy_(torch.exp(0.1 * z) / (64.0 * math.sqrt(s[1])))
+                    m, ex = torch.frexp(sc)                  # sc = m * 2^ex, m in [0.5, 1)
+                    sc = torch.ldexp(torch.ones_like(sc), torch.where(m == 0.5, ex - 1, ex))
+                sc = torch.where(amax > 0, sc, torch.ones_like(sc))
+                full = sc.repeat_interleave(FP8_BLOCK, dim=1)[:, :s[1]]
+                codes[w][j].copy_((wf / full).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn))
+                scales[w][j].copy_(sc)
         return ExpertWeights(codes[0], codes[1], codes[2], scales[0], scales[1], scales[2],
                              dtype="fp8", scales_pow2=cfg.w_scales == "pow2")
     raise ValueError(cfg.w_dtype)
