@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = ["MoeError", "lib", "library_path", "moe_version", "moe_route",
-           "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch",
+           "moe_layout_workspace_bytes", "moe_layout", "moe_layout_noalloc", "moe_dispatch",
            "moe_ffn_workspace_bytes", "moe_ffn_gate_up", "moe_ffn_down",
            "moe_grouped_ffn", "moe_combine", "moe_layout_masked", "moe_ffn_gate_up_masked",
            "moe_ffn_down_masked", "moe_grouped_ffn_masked", "moe_route_mapped", "moe_eplb_place", "moe_route_shared",
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         "moe_route": ([P, I, I, I, P, P, P], S),
         "moe_layout_workspace_bytes": ([I, I, I], Z),
         "moe_layout": ([P, I, I, I, I, I, P, P, P, P, I, P, Z, P], S),
+        "moe_layout_noalloc": ([P, I, I, I, I, I, P, P, P, P, I, P], S),
         "moe_dispatch": ([P, P, I, I, I, P, I, P, I, P, I, P], S),
         "moe_ffn_workspace_bytes": ([I, I, I], Z),
         "moe_ffn_gate_up": ([P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, P], S),
@@ -218,6 +219,31 @@ def moe_layout(topk_ids, E: int, e_begin: int, e_end: int, cap_rows: int, counts
     _check(lib().moe_layout(_ptr(topk_ids), B, K, E, e_begin, e_end, _ptr(counts), _ptr(offsets),
                             _ptr(row_of), _ptr(src_of), cap_rows, _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)))
+    return {"counts": counts, "offsets": offsets, "row_of": row_of, "src_of": src_of}
+
+
+LAYOUT_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def moe_layout_noalloc(topk_ids, E: int, e_begin: int, e_end: int, cap_rows: int, counts=None,
+                       offsets=None, row_of=None, src_of=None, stream=None) -> dict:
+    """moe_layout without a workspace argument: the library's own per-GPU
+    scratch (LAYOUT_NOALLOC_SCRATCH_BYTES) holds the chunk histograms, and
+    the call allocates nothing on the device when every output is given.
+    Batches needing more workspace than that raise MoeError; calls that
+    overlap on one GPU race on the shared scratch."""
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    B, K = topk_ids.shape
+    dev = topk_ids.device
+    E_loc = e_end - e_begin
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(max(E_loc, 0) + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_of = torch.empty((B, K), dtype=torch.int32, device=dev) if row_of is None else row_of
+    src_of = torch.empty(max(cap_rows, 1), dtype=torch.int32, device=dev) if src_of is None else src_of
+    for n, t in (("counts", counts), ("offsets", offsets), ("row_of", row_of), ("src_of", src_of)):
+        _dev(t, n, torch.int32)
+    _check(lib().moe_layout_noalloc(_ptr(topk_ids), B, K, E, e_begin, e_end, _ptr(counts), _ptr(offsets),
+                                    _ptr(row_of), _ptr(src_of), cap_rows, _stream(stream)))
     return {"counts": counts, "offsets": offsets, "row_of": row_of, "src_of": src_of}
 
 

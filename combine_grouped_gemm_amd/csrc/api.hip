@@ -8,6 +8,9 @@
 #include "launch.hpp"
 #include "moeep.h"
 
+static_assert(MOE_LAYOUT_NOALLOC_SCRATCH_BYTES == moeep::kLayoutScratchBytes,
+              "the header states the library's layout scratch size");
+
 namespace moeep {
 
 int device_cu_count() {
@@ -280,6 +283,32 @@ moe_status_t moe_layout(const int32_t* topk_ids, int B, int K, int E, int e_begi
     return launched(moeep::launch_layout(topk_ids, B, K, E, e_begin, e_end, counts, offsets, row_of,
                                          src_of, cap_rows, ws, stream),
                     "moe_layout");
+}
+
+moe_status_t moe_layout_noalloc(const int32_t* topk_ids, int B, int K, int E, int e_begin, int e_end,
+                                int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                                int cap_rows, hipStream_t stream) {
+    moe_status_t s = check_route_shape(B, E, K);
+    if (s != MOE_OK) return s;
+    REQUIRE(e_begin >= 0 && e_begin < e_end && e_end <= E,
+            "need 0 <= e_begin < e_end <= E (got %d, %d, E=%d)", e_begin, e_end, E);
+    REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
+    REQUIRE(counts && offsets, "null counts or offsets");
+    if (B > 0) REQUIRE(topk_ids && row_of, "null topk_ids or row_of");
+    if (cap_rows > 0) REQUIRE(src_of, "null src_of");
+    const size_t need = moeep::layout_workspace_bytes(B, K, E);
+    REQUIRE(need <= moeep::kLayoutScratchBytes,
+            "moe_layout_noalloc: B=%d, K=%d, E=%d needs %zu bytes of layout workspace, more than the "
+            "library's %zu (use moe_layout with a caller workspace)",
+            B, K, E, need, moeep::kLayoutScratchBytes);
+    void* ws = nullptr;
+    const hipError_t e = moeep::layout_scratch_ptr(&ws);
+    if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, "moe_layout_noalloc: no device address for the layout scratch: %s",
+                    hipGetErrorString(e));
+    return launched(moeep::launch_layout(topk_ids, B, K, E, e_begin, e_end, counts, offsets, row_of,
+                                         src_of, cap_rows, ws, stream),
+                    "moe_layout_noalloc");
 }
 
 moe_status_t moe_layout_masked(const int32_t* topk_ids, int B, int K, int E, int e_begin, int e_end,

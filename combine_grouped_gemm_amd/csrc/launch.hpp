@@ -19,6 +19,12 @@ bool place_experts(const int64_t* load, int E, int G, int32_t* phys_of_logical);
 
 // layout.hip
 size_t layout_workspace_bytes(int B, int K, int E);
+// moe_layout_noalloc: the layout workspace held by the library, one
+// kLayoutScratchBytes array per GPU; layout_scratch_ptr gives the current
+// GPU's copy (its device address, looked up once per GPU and cached)
+constexpr size_t kLayoutScratchBytes = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t layout_scratch_ptr(void** out);
 hipError_t launch_layout(const int32_t* ids, int B, int K, int E, int e_begin, int e_end,
                          int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
                          int cap, void* ws, hipStream_t stream);

@@ -36,8 +36,17 @@
 // local expert j owns rows [j*cap_e, (j+1)*cap_e), so the ranking needs no
 // offsets: a slot's row is j*cap_e + its rank within the expert, slots with
 // rank >= cap_e are dropped, and the scan also writes m[j] = min(count, cap_e).
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
+
+// Library-held workspace of the layout kernels for callers that cannot
+// allocate (moe_layout_noalloc): the chunk histograms of one call.  One copy
+// per GPU, alive until the process ends.  Host code never passes this name to
+// a kernel (on the host it is only a stand-in for the symbol): it uses the
+// device address hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) unsigned char scratch[moeep::kLayoutScratchBytes];
 
 namespace moeep {
 namespace {
@@ -290,6 +299,25 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
 }
 
 }  // namespace
+
+hipError_t layout_scratch_ptr(void** out) {
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
+}
 
 size_t layout_workspace_bytes(int B, int K, int E) {
     const int nchunk = n_chunks((long long)B * K);

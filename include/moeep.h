@@ -174,6 +174,29 @@ moe_status_t moe_layout(const int32_t* topk_ids, int B, int K, int E, int e_begi
                         int cap_rows, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_layout_noalloc -- moe_layout for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results minus the workspace,
+ * which the library holds itself as one static device array of
+ * MOE_LAYOUT_NOALLOC_SCRATCH_BYTES per GPU (kept until the process ends).
+ * Calls no hipMalloc or hipFree.  A batch whose workspace
+ * (moe_layout_workspace_bytes(B, K, E)) exceeds that size is rejected with
+ * MOE_ERR_INVALID_ARG before anything is enqueued: 4 MiB holds E * ceil(B*K
+ * / 256) int32 chunk histograms, e.g. E = 256 up to B*K = 1,048,320 slots
+ * (the T = 8192, K = 8 prefill needs 256 KiB); batches of at most 4096 slots
+ * use no workspace at all.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and must be
+ * serialised by the caller.  Nothing in the array has to start at zero: each
+ * call writes every histogram entry it reads.  The first call on a GPU looks
+ * up the array's device address for that GPU (hipGetSymbolAddress) with the
+ * caller's device current; a failure there returns MOE_ERR_HIP.
+ */
+#define MOE_LAYOUT_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status_t moe_layout_noalloc(const int32_t* topk_ids, int B, int K, int E, int e_begin, int e_end,
+                                int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                                int cap_rows, hipStream_t stream);
+
+/*
  * moe_layout_masked -- the fixed-capacity ("masked") layout.  [SGLang]
  * MoE-runner table: the grouped GEMM takes a contiguous layout for prefill
  * and a masked layout for decode; the dispatch paragraph pairs the

@@ -159,3 +159,23 @@ def test_route_shared_rejects():
     assert "n_shared" in L.moe_last_error().decode()
     assert L.moe_route_shared(p, 4, 16, 2, -1, p, p, None) == m.MOE_ERR_INVALID_ARG
     assert L.moe_route_shared(None, 0, 16, 2, 1, None, None, None) == m.MOE_OK
+
+
+def test_layout_noalloc_rejects_before_any_hip_call():
+    """The allocation-free layout checks everything on the host first: a batch
+    whose chunk histograms exceed the library's scratch is refused with a
+    message naming the limit, before the scratch is looked up."""
+    L = m.lib()
+    p = ctypes.c_void_p(256)
+    limit = m.LAYOUT_NOALLOC_SCRATCH_BYTES
+    # E = 1024, B*K = 2^20 slots: 4096 chunks x 1024 experts x 4 bytes = 16 MiB
+    assert L.moe_layout_workspace_bytes(1 << 17, 8, 1024) > limit
+    assert L.moe_layout_noalloc(p, 1 << 17, 8, 1024, 0, 1024, p, p, p, p, 1 << 20, None) == \
+        m.MOE_ERR_INVALID_ARG
+    msg = L.moe_last_error().decode()
+    assert "moe_layout_noalloc" in msg and str(limit) in msg
+    assert L.moe_layout_noalloc(p, 4, 2, 8, 5, 5, p, p, p, p, 8, None) == m.MOE_ERR_INVALID_ARG
+    assert "e_begin" in L.moe_last_error().decode()
+    assert L.moe_layout_noalloc(p, 4, 2, 8, 0, 8, None, p, p, p, 8, None) == m.MOE_ERR_INVALID_ARG
+    # the prefill batch (T = 8192, K = 8, E = 256) fits
+    assert L.moe_layout_workspace_bytes(8192, 8, 256) <= limit
