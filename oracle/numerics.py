@@ -71,7 +71,18 @@ def block_scale_pow2(amax):
     return out
 
 
-def quantize_fp8_blocks(v, block: int = FP8_BLOCK):
+def block_scale_amax(amax):
+    """The alternative block scale s = amax / 448 in fp32 (1 when amax = 0):
+    the block's largest magnitude lands exactly on the largest e4m3 code.  Not
+    used by the layer (its activation scales are powers of two, see
+    block_scale_pow2); kept to measure what that choice costs in precision."""
+    amax = np.asarray(amax, dtype=np.float32)
+    with np.errstate(under="ignore"):
+        s = (amax / np.float32(448.0)).astype(np.float32)
+    return np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+
+
+def quantize_fp8_blocks(v, block: int = FP8_BLOCK, rule: str = "pow2"):
     """Block-wise fp8 quantisation along the last axis.
 
     For each run of ``block`` consecutive elements (the last run may be
@@ -85,7 +96,12 @@ def quantize_fp8_blocks(v, block: int = FP8_BLOCK):
     Returns (codes, scales): codes are fp64 values on the e4m3 grid with the
     shape of ``v``; scales are fp32 with the last axis replaced by the number
     of blocks.  The represented value is codes * scales (per block).
+    rule = 'amax448' takes s = block_scale_amax(amax) instead (the division
+    is then an fp32 division that rounds).
     """
+    if rule not in ("pow2", "amax448"):
+        raise ValueError(f"unknown scale rule {rule!r}")
+    scale_of = block_scale_pow2 if rule == "pow2" else block_scale_amax
     v32 = np.asarray(v, dtype=np.float32)
     n = v32.shape[-1]
     nb = -(-n // block)
@@ -94,7 +110,7 @@ def quantize_fp8_blocks(v, block: int = FP8_BLOCK):
     for b in range(nb):
         blk = v32[..., b * block:(b + 1) * block]
         amax = np.max(np.abs(blk), axis=-1)
-        s = block_scale_pow2(amax)
+        s = scale_of(amax)
         with np.errstate(over="ignore", under="ignore"):
             ratio = (blk / s[..., None]).astype(np.float32)   # fp32 division
         codes[..., b * block:(b + 1) * block] = to_e4m3_sat(ratio.astype(np.float64))
@@ -110,17 +126,17 @@ def dequantize_fp8_blocks(codes, scales, block: int = FP8_BLOCK) -> np.ndarray:
     return codes * s
 
 
-def round_act(v, dtype: str):
+def round_act(v, dtype: str, rule: str = "pow2"):
     """Round activations to the storage type named by ``dtype``.
 
     'f32' and 'bf16' return fp64 values on that grid; 'fp8' returns the
-    (codes, scales) pair of :func:`quantize_fp8_blocks` taken on the fp32
-    rounding of ``v``.
+    (codes, scales) pair of :func:`quantize_fp8_blocks` (scale rule ``rule``)
+    taken on the fp32 rounding of ``v``.
     """
     if dtype == "f32":
         return to_f32(v)
     if dtype == "bf16":
         return to_bf16(v)
     if dtype == "fp8":
-        return quantize_fp8_blocks(to_f32(v))
+        return quantize_fp8_blocks(to_f32(v), rule=rule)
     raise ValueError(f"unknown dtype {dtype!r}")

@@ -95,3 +95,25 @@ def test_round_to_grid_subnormals():
     # e4m3 smallest subnormal is 2^-9
     assert nx.to_e4m3_sat(2.0**-10) == 0.0
     assert nx.to_e4m3_sat(3 * 2.0**-10) == 2.0**-8
+
+
+def test_block_scale_amax_rule_by_hand():
+    """The alternative scale rule s = amax / 448 (fp32; 1 for an all-zero
+    block): 448 -> 1, 896 -> 2, 0 -> 1, 1 -> fp32(1/448); quantising with it
+    puts each block's largest magnitude on the top code 448 (the division
+    rounds in fp32, so within one code of it) and the pow2 rule's scale is
+    never smaller."""
+    s = nx.block_scale_amax([448.0, 896.0, 0.0, 1.0])
+    assert s.dtype == np.float32
+    assert list(s[:3]) == [1.0, 2.0, 1.0]
+    assert s[3] == np.float32(1.0) / np.float32(448.0)
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((5, 300)) * np.exp(rng.standard_normal((5, 1)))
+    codes, sc = nx.quantize_fp8_blocks(v, rule="amax448")
+    for b in range(3):
+        top = np.max(np.abs(codes[:, b * 128:(b + 1) * 128]), axis=1)
+        assert np.all((top == 448.0) | (top == 416.0)), top
+    _, sp = nx.quantize_fp8_blocks(v)
+    assert np.all(sp >= sc)
+    with pytest.raises(ValueError):
+        nx.quantize_fp8_blocks(v, rule="other")

@@ -232,6 +232,23 @@ def _expert_generator(cfg: MoEConfig, e_global: int, which: int, device) -> torc
     return g
 
 
+def _draw_fp32(cfg: MoEConfig, e_global: int, which: int, shape, device) -> torch.Tensor:
+    """Matrix `which` (0 gate, 1 up, 2 down) of expert e_global, fp32
+    N(0, 1/fan_in) with fan_in = shape[1]."""
+    g = _expert_generator(cfg, e_global, which, device)
+    return torch.randn(shape, generator=g, device=device) / math.sqrt(shape[1])
+
+
+def gen_expert_weights_fp32(cfg: MoEConfig, device="cpu", experts=None) -> ExpertWeights:
+    """The fp32 weights an fp8 workload's codes and scales are quantised from
+    (the same draws as gen_expert_weights), for measuring what quantisation
+    costs.  gate, up (E_loc, I, H); down (E_loc, H, I)."""
+    experts = list(range(cfg.e_begin, cfg.e_end)) if experts is None else [int(e) for e in experts]
+    shapes = ((cfg.I, cfg.H), (cfg.I, cfg.H), (cfg.H, cfg.I))
+    mats = [torch.stack([_draw_fp32(cfg, e, w, s, device) for e in experts]) for w, s in enumerate(shapes)]
+    return ExpertWeights(*mats, dtype="f32")
+
+
 def gen_expert_weights(cfg: MoEConfig, device="cpu", experts=None) -> ExpertWeights:
     """Expert weights drawn on ``device``, N(0, 1/fan_in) in value.
 
@@ -272,8 +289,7 @@ def gen_expert_weights(cfg: MoEConfig, device="cpu", experts=None) -> ExpertWeig
             scales.append(torch.empty((E_loc, s[0], nb), dtype=torch.float32, device=device))
         for j, e in enumerate(experts):
             for w, s in enumerate(shapes):
-                g = _expert_generator(cfg, e, w, device)
-                wf = torch.randn(s, generator=g, device=device) / math.sqrt(s[1])
+                wf = _draw_fp32(cfg, e, w, s, device)
                 nb = scales[w].shape[2]
                 pad = nb * FP8_BLOCK - s[1]
                 amax = torch.nn.functional.pad(wf.abs(), (0, pad)).view(s[0], nb, FP8_BLOCK).amax(dim=2)
