@@ -119,6 +119,18 @@ def _dev(t, name, dtype=None, ndim=None):
     return t
 
 
+def _need(t, name, numel=None, shape=None):
+    """Caller-provided tensors must cover what the kernels index: the C ABI
+    cannot see sizes, so an undersized tensor would be written out of bounds
+    on the device.  Raises ValueError before any library call."""
+    if t is None:
+        return
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements (got {t.numel()})")
+
+
 def _dtype_code(d):
     if isinstance(d, str):
         return _NAMES[d]
@@ -142,6 +154,8 @@ def moe_route(logits, K: int, topk_ids=None, topk_w=None, stream=None):
         topk_w = torch.empty((B, K), dtype=torch.float32, device=logits.device)
     _dev(topk_ids, "topk_ids", torch.int32)
     _dev(topk_w, "topk_w", torch.float32)
+    _need(topk_ids, "topk_ids", shape=(B, K))
+    _need(topk_w, "topk_w", shape=(B, K))
     _check(lib().moe_route(_ptr(logits), B, E, K, _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
     return topk_ids, topk_w
 
@@ -160,6 +174,8 @@ def moe_route_mapped(logits, K: int, phys_of_logical, topk_ids=None, topk_w=None
         topk_w = torch.empty((B, K), dtype=torch.float32, device=logits.device)
     _dev(topk_ids, "topk_ids", torch.int32, 2)
     _dev(topk_w, "topk_w", torch.float32, 2)
+    _need(topk_ids, "topk_ids", shape=(B, K))
+    _need(topk_w, "topk_w", shape=(B, K))
     _check(lib().moe_route_mapped(_ptr(logits), B, E, K, _ptr(phys_of_logical), _ptr(topk_ids),
                                   _ptr(topk_w), _stream(stream)))
     return topk_ids, topk_w
@@ -199,6 +215,13 @@ def moe_layout_workspace_bytes(B: int, K: int, E: int) -> int:
     return int(lib().moe_layout_workspace_bytes(B, K, E))
 
 
+def _check_layout_outputs(B, K, E, E_loc, cap_rows, counts, offsets, row_of, src_of):
+    _need(counts, "counts", numel=E)
+    _need(offsets, "offsets", numel=max(E_loc, 0) + 1)
+    _need(row_of, "row_of", numel=B * K)
+    _need(src_of, "src_of", numel=cap_rows)
+
+
 def moe_layout(topk_ids, E: int, e_begin: int, e_end: int, cap_rows: int, counts=None,
                offsets=None, row_of=None, src_of=None, ws=None, stream=None) -> dict:
     """counts (E), offsets (E_loc+1), row_of (B, K), src_of (cap_rows), all int32."""
@@ -215,6 +238,7 @@ def moe_layout(topk_ids, E: int, e_begin: int, e_end: int, cap_rows: int, counts
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     for n, t in (("counts", counts), ("offsets", offsets), ("row_of", row_of), ("src_of", src_of)):
         _dev(t, n, torch.int32)
+    _check_layout_outputs(B, K, E, E_loc, cap_rows, counts, offsets, row_of, src_of)
     _dev(ws, "ws")
     _check(lib().moe_layout(_ptr(topk_ids), B, K, E, e_begin, e_end, _ptr(counts), _ptr(offsets),
                             _ptr(row_of), _ptr(src_of), cap_rows, _ptr(ws),
@@ -242,6 +266,7 @@ def moe_layout_noalloc(topk_ids, E: int, e_begin: int, e_end: int, cap_rows: int
     src_of = torch.empty(max(cap_rows, 1), dtype=torch.int32, device=dev) if src_of is None else src_of
     for n, t in (("counts", counts), ("offsets", offsets), ("row_of", row_of), ("src_of", src_of)):
         _dev(t, n, torch.int32)
+    _check_layout_outputs(B, K, E, E_loc, cap_rows, counts, offsets, row_of, src_of)
     _check(lib().moe_layout_noalloc(_ptr(topk_ids), B, K, E, e_begin, e_end, _ptr(counts), _ptr(offsets),
                                     _ptr(row_of), _ptr(src_of), cap_rows, _stream(stream)))
     return {"counts": counts, "offsets": offsets, "row_of": row_of, "src_of": src_of}
@@ -265,6 +290,10 @@ def moe_layout_masked(topk_ids, E: int, e_begin: int, e_end: int, cap_per_expert
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     for n, t in (("counts", counts), ("m", m), ("row_of", row_of), ("src_of", src_of)):
         _dev(t, n, torch.int32)
+    _need(counts, "counts", numel=E)
+    _need(m, "m", numel=max(E_loc, 0))
+    _need(row_of, "row_of", numel=B * K)
+    _need(src_of, "src_of", numel=max(E_loc, 0) * cap_per_expert)
     _dev(ws, "ws")
     _check(lib().moe_layout_masked(_ptr(topk_ids), B, K, E, e_begin, e_end, _ptr(counts), _ptr(m),
                                    _ptr(row_of), _ptr(src_of), cap_per_expert, _ptr(ws),
@@ -296,6 +325,14 @@ def moe_dispatch(seg_x, row_of, cap_rows: int, xd_dtype=None, xd=None, xd_scales
     if xd_code == MOE_FP8_E4M3 and xd_scales is None:
         xd_scales = torch.empty((max(cap_rows, 1), -(-H // FP8_BLOCK)), dtype=torch.float32, device=dev)
     _dev(xd, "xd")
+    B = sum(int(t.shape[0]) for t in seg_x)
+    _need(row_of, "row_of", shape=(B, K))
+    if xd.dtype != _TORCH[xd_code]:
+        raise ValueError(f"xd must be {_TORCH[xd_code]} (got {xd.dtype})")
+    _need(xd, "xd", numel=cap_rows * H)
+    if xd_code == MOE_FP8_E4M3:
+        _dev(xd_scales, "xd_scales", torch.float32)
+        _need(xd_scales, "xd_scales", numel=cap_rows * (-(-H // FP8_BLOCK)))
     ptrs = (ctypes.c_void_p * len(seg_x))(*[s.data_ptr() for s in seg_x])
     rows = (ctypes.c_int32 * len(seg_x))(*[s.shape[0] for s in seg_x])
     _check(lib().moe_dispatch(ctypes.cast(ptrs, ctypes.c_void_p), ctypes.cast(rows, ctypes.c_void_p),
@@ -329,6 +366,29 @@ def _rows_arg(rows, cap_per_expert, E_loc, n_rows):
     return int(cap_per_expert)
 
 
+def _check_ffn(a, a_scales, rows, cap_per_expert, E_loc, Kdim, cap, act, **tensors):
+    """Shapes of the FFN operands: the activation rows (cap, Kdim) [+ fp8
+    scales], the row description (offsets E_loc + 1, or m E_loc), and each
+    named (tensor, shape or minimum element count) pair."""
+    if a.shape[1] != Kdim:
+        raise ValueError(f"activations must have {Kdim} columns (got {a.shape[1]})")
+    _need(rows, "offsets" if cap_per_expert is None else "m",
+          numel=E_loc + 1 if cap_per_expert is None else E_loc)
+    if act == MOE_FP8_E4M3:
+        if a_scales is None:
+            raise ValueError("fp8 activations need their block scales")
+        _dev(a_scales, "activation scales", torch.float32)
+        _need(a_scales, "activation scales", numel=cap * (-(-Kdim // FP8_BLOCK)))
+    for name, (t, want) in tensors.items():
+        if t is None:
+            continue
+        _dev(t, name)
+        if isinstance(want, tuple):
+            _need(t, name, shape=want)
+        else:
+            _need(t, name, numel=want)
+
+
 def _w_code(act, w_scales_pow2):
     """Weight dtype code: fp8 weights whose block scales are all powers of two
     are declared as MOE_FP8_E4M3_PO2."""
@@ -356,6 +416,15 @@ def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_
         h = torch.empty((cap, I), dtype=xd.dtype, device=xd.device)
     if act == MOE_FP8_E4M3 and h_scales is None:
         h_scales = torch.empty((cap, -(-I // FP8_BLOCK)), dtype=torch.float32, device=xd.device)
+    if h.dtype != xd.dtype:
+        raise ValueError(f"h must be {xd.dtype} (got {h.dtype})")
+    nbH, nbI = -(-H // FP8_BLOCK), -(-I // FP8_BLOCK)
+    fp8 = act == MOE_FP8_E4M3
+    _check_ffn(xd, xd_scales, offsets, cap_per_expert, E_loc, H, cap, act,
+               w_up=(w_up, (E_loc, I, H)), h=(h, cap * I),
+               h_scales=(h_scales if fp8 else None, cap * nbI),
+               w_gate_scales=(w_gate_scales if fp8 else None, (E_loc, I, nbH)),
+               w_up_scales=(w_up_scales if fp8 else None, (E_loc, I, nbH)))
     fn = lib().moe_ffn_gate_up if cap_per_expert is None else lib().moe_ffn_gate_up_masked
     _check(fn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, third, H, I, act,
               _ptr(w_gate), _ptr(w_up), _ptr(w_gate_scales), _ptr(w_up_scales),
@@ -380,6 +449,9 @@ def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dty
     y_dtype = _y_dtype_for(act) if y_dtype is None else y_dtype
     if y is None:
         y = torch.empty((cap, H), dtype=y_dtype, device=h.device)
+    fp8 = act == MOE_FP8_E4M3
+    _check_ffn(h, h_scales, offsets, cap_per_expert, E_loc, I, cap, act, y=(y, cap * H),
+               w_down_scales=(w_down_scales if fp8 else None, (E_loc, H, -(-I // FP8_BLOCK))))
     fn = lib().moe_ffn_down if cap_per_expert is None else lib().moe_ffn_down_masked
     _check(fn(_ptr(h), _ptr(h_scales), _ptr(offsets), E_loc, third, H, I, act,
               _ptr(w_down), _ptr(w_down_scales), _w_code(act, w_scales_pow2), _ptr(y), _DT[y.dtype],
@@ -405,6 +477,13 @@ def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=
     need = moe_ffn_workspace_bytes(cap, I, act)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=xd.device)
+    fp8 = act == MOE_FP8_E4M3
+    nbH, nbI = -(-H // FP8_BLOCK), -(-I // FP8_BLOCK)
+    _check_ffn(xd, xd_scales, offsets, cap_per_expert, E_loc, H, cap, act,
+               w_up=(w_up, (E_loc, I, H)), w_down=(w_down, (E_loc, H, I)), y=(y, cap * H),
+               w_gate_scales=(w_gate_scales if fp8 else None, (E_loc, I, nbH)),
+               w_up_scales=(w_up_scales if fp8 else None, (E_loc, I, nbH)),
+               w_down_scales=(w_down_scales if fp8 else None, (E_loc, H, nbI)))
     fn = lib().moe_grouped_ffn if cap_per_expert is None else lib().moe_grouped_ffn_masked
     _check(fn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, third, H, I, act,
               _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
@@ -439,6 +518,8 @@ def moe_combine(y, row_of, topk_w, out=None, out_dtype=None, stream=None):
     if out is None:
         out = torch.empty((B, H), dtype=y.dtype if out_dtype is None else out_dtype, device=y.device)
     _dev(out, "out")
+    _need(topk_w, "topk_w", shape=(B, K))
+    _need(out, "out", numel=B * H)
     _check(lib().moe_combine(_ptr(y), _DT[y.dtype], y.shape[0], _ptr(row_of), _ptr(topk_w), B, K, H,
                              _ptr(out), _DT[out.dtype], _stream(stream)))
     return out
