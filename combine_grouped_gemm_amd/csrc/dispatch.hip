@@ -10,8 +10,11 @@
 // row; a row of at most 448 vectors is one block of whole waves): each
 // thread reads one vector from HBM once and writes it to every local
 // destination row of the token, so a decode-sized batch still spreads over
-// the whole chip.  A token with no slot on the local experts is not read at
-// all.  Plain stores: the non-temporal hint made this kernel slower in the
+// the whole chip.  The token's destination rows are read with one vector
+// load per wave (lane k holds slot k's row; a ballot gives the local slots)
+// instead of a chain of dependent scalar loads ahead of the row load (EP
+// share 28 -> 23 us).  A token with no slot on the local experts is not read
+// at all.  Plain stores: the non-temporal hint made this kernel slower in the
 // layer's sequence.  For fp8 storage the token is quantised once per
 // 128-element block (the 16 lanes of a DPP row cover a block; amax by
 // cross-lane moves inside the row) and every copy receives the same codes
@@ -31,19 +34,30 @@ inline int dispatch_threads(int nvec) {
     return w < kDispThreads ? w : kDispThreads;
 }
 
-// Whether token t has a slot on the local experts (uniform over the block).
-__device__ __forceinline__ bool has_local_slot(const int32_t* rows, int K, int cap) {
-    for (int k = 0; k < K; ++k) {
-        const int r = rows[k];
-        if (r >= 0 && r < cap) return true;
-    }
-    return false;
+// Slots [k0, k0 + 64) of a token, one per lane: lane l holds row_of[t, k0 + l]
+// when that slot exists and its row is in this buffer, else -1.  One vector
+// load per wave, so no chain of dependent scalar loads precedes the token row.
+__device__ __forceinline__ int slot_row(const int32_t* rows, int K, int k0, int cap, int lane) {
+    const int k = k0 + lane;
+    if (k >= K) return -1;
+    const int r = rows[k];
+    return (r >= 0 && r < cap) ? r : -1;
 }
 
+// Rows of token t in the segment-major concatenation: its segment is the
+// number of segment starts at or below t (independent compares, no early exit).
 __device__ __forceinline__ const void* token_row(const SegTable& seg, int t, size_t row_bytes) {
     int i = 0;
-    while (i + 1 < seg.n && t >= seg.start[i + 1]) ++i;
+    for (int s = 1; s < seg.n; ++s) i += t >= seg.start[s] ? 1 : 0;
     return static_cast<const char*>(seg.ptr[i]) + (size_t)(t - seg.start[i]) * row_bytes;
+}
+
+// Whether any slot of the token is local (uniform over the block), looking at
+// 64 slots per vector load.
+__device__ __forceinline__ bool any_local(const int32_t* rows, int K, int cap, int lane) {
+    for (int k0 = 0; k0 < K; k0 += kWave)
+        if (ballot64(slot_row(rows, K, k0, cap, lane) >= 0) != 0) return true;
+    return false;
 }
 
 // 16-byte copies (f32 -> f32, bf16 -> bf16).
@@ -52,13 +66,24 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_copy_kernel(
     char* __restrict__ xd) {
     const int t = blockIdx.x;
     const int c = blockIdx.y * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x % kWave;
     const int nvec = (int)(row_bytes / 16);
     const int32_t* rows = row_of + (size_t)t * K;
-    if (c >= nvec || !has_local_slot(rows, K, cap)) return;
+    int my = slot_row(rows, K, 0, cap, lane);
+    uint64_t m = ballot64(my >= 0);          // local slots among the first 64, the same in every wave
+    if ((m == 0 && (K <= kWave || !any_local(rows, K, cap, lane))) || c >= nvec) return;
     const uint4 v = static_cast<const uint4*>(token_row(seg, t, row_bytes))[c];
-    for (int k = 0; k < K; ++k) {
-        const int r = rows[k];
-        if (r >= 0 && r < cap) reinterpret_cast<uint4*>(xd + (size_t)r * row_bytes)[c] = v;
+    for (int k0 = 0;;) {
+        while (m != 0) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const int r = __builtin_amdgcn_readlane(my, k);
+            reinterpret_cast<uint4*>(xd + (size_t)r * row_bytes)[c] = v;
+        }
+        k0 += kWave;
+        if (k0 >= K) break;
+        my = slot_row(rows, K, k0, cap, lane);
+        m = ballot64(my >= 0);
     }
 }
 
@@ -70,10 +95,14 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
     uint8_t* __restrict__ xd, float* __restrict__ xd_scales) {
     const int t = blockIdx.x;
     const int c = blockIdx.y * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x % kWave;
     const int nvec = H / 8;                 // 8 bf16 per 16-byte vector
     const int nblk = (H + 127) / 128;
     const int32_t* rows = row_of + (size_t)t * K;
-    if (!has_local_slot(rows, K, cap)) return;      // whole block: the DPP rows below stay complete
+    int my = slot_row(rows, K, 0, cap, lane);
+    uint64_t m = ballot64(my >= 0);
+    // whole block: the DPP rows below stay complete
+    if (m == 0 && (K <= kWave || !any_local(rows, K, cap, lane))) return;
     const bool ok = c < nvec;
     const uint4* src = static_cast<const uint4*>(token_row(seg, t, (size_t)H * 2));
     const uint4 v = ok ? src[c] : make_uint4(0, 0, 0, 0);
@@ -89,11 +118,18 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
     // |f * rs| <= amax / s <= 448, the range where the hardware conversion is exact RNE
     const uint32_t lo = e4m3_pair(f[0] * rs, f[1] * rs) | (e4m3_pair(f[2] * rs, f[3] * rs) << 16);
     const uint32_t hi = e4m3_pair(f[4] * rs, f[5] * rs) | (e4m3_pair(f[6] * rs, f[7] * rs) << 16);
-    for (int k = 0; k < K; ++k) {
-        const int r = rows[k];
-        if (r < 0 || r >= cap) continue;
-        reinterpret_cast<uint2*>(xd + (size_t)r * H)[c] = make_uint2(lo, hi);
-        if ((c & 15) == 0) xd_scales[(size_t)r * nblk + c / 16] = s;
+    for (int k0 = 0;;) {
+        while (m != 0) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const int r = __builtin_amdgcn_readlane(my, k);
+            reinterpret_cast<uint2*>(xd + (size_t)r * H)[c] = make_uint2(lo, hi);
+            if ((c & 15) == 0) xd_scales[(size_t)r * nblk + c / 16] = s;
+        }
+        k0 += kWave;
+        if (k0 >= K) break;
+        my = slot_row(rows, K, k0, cap, lane);
+        m = ballot64(my >= 0);
     }
 }
 

@@ -50,6 +50,8 @@ SMALL = [
     # more than 8 slots per token: combine gathers in passes of 8 slots (two and three passes)
     wl.scaled(C["dsv3_decode"], "decode_k12", seg_rows=(48,), E=32, K=12, H=256, I=128),
     wl.scaled(C["dsv3_prefill"], "prefill_k20", seg_rows=(40,), E=64, K=20, H=128, I=64),
+    # more than 64 slots per token: dispatch and combine read the slot rows 64 at a time
+    wl.scaled(C["dsv3_decode"], "decode_k70", seg_rows=(20,), E=128, K=70, H=128, I=64),
     # the single-workgroup layout's limit: 4096 slots (four 1024-slot chunks) and just past
     # it (the three-kernel layout), on a partial expert range
     wl.scaled(C["ep8_share"], "layout_4096_slots", seg_rows=(300, 212), E=32, K=8, H=128, I=64,
