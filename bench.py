@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--cold-mb", type=int, default=512,
                     help="rotate buffer sets until they exceed this many MB (0: one set, warm only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense-weights", action="store_true",
+                    help="feed the FFN the weights in their dense (out, in) layout instead of packing them "
+                         "once (untimed) to the library's padded row pitch")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="target CPU seconds for the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -407,6 +410,11 @@ def run_workload(m, cfg, a, dev, copy_gbs, headline):
     else:
         W = wl.gen_expert_weights(cfg, device=dev)
     wdict = W.as_dict()
+    if not a.dense_weights:
+        # once, before any timing, as a weight loader would: rows at the packed pitch
+        for k in ("gate", "up", "down"):
+            wdict[k] = m.moe_pack_weights(wdict[k])
+        torch.cuda.synchronize()
     layout = a.layout if headline else "contiguous"
     n_shared = a.shared_experts if headline else 0
 
@@ -483,6 +491,7 @@ def run_workload(m, cfg, a, dev, copy_gbs, headline):
               "local_experts": [cfg.e_begin, cfg.e_end], "segments": len(cfg.seg_rows),
               "rows": R, "experts_touched": touched,
               "buffer_sets": n_sets, "buffer_set_MB": round(per_set / 2**20, 1),
+              "weights": "dense" if a.dense_weights else "packed",
               **({"weight_scales": cfg.w_scales} if cfg.w_dtype == "fp8" else {})}
     if not headline:
         out = {"value": round(cfg.T / (ms_cold / 1e3), 1), "unit": "tokens/s",

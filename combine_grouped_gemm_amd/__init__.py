@@ -21,11 +21,13 @@ __all__ = ["MoeError", "lib", "library_path", "moe_version", "moe_route",
            "moe_ffn_workspace_bytes", "moe_ffn_gate_up", "moe_ffn_down",
            "moe_grouped_ffn", "moe_combine", "moe_layout_masked", "moe_ffn_gate_up_masked",
            "moe_ffn_down_masked", "moe_grouped_ffn_masked", "moe_route_mapped", "moe_eplb_place", "moe_route_shared",
-           "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_FP8_E4M3_PO2",
+           "moe_weight_ld", "moe_packed_weight_bytes", "moe_pack_weights",
+           "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_FP8_E4M3_PO2", "MOE_W_PACKED",
            "MoELayer"]
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP8_E4M3_PO2 = 0, 1, 2, 3
+MOE_W_PACKED = 0x100
 FP8_BLOCK = 128
 MAX_SEGMENTS = 64
 
@@ -76,6 +78,9 @@ def lib() -> ctypes.CDLL:
         "moe_route_mapped": ([P, I, I, I, P, P, P, P], S),
         "moe_eplb_place": ([P, I, I, P], S),
         "moe_route_shared": ([P, I, I, I, I, P, P, P], S),
+        "moe_weight_ld": ([I, I], I),
+        "moe_packed_weight_bytes": ([I, I, I, I], Z),
+        "moe_pack_weights": ([P, I, I, I, I, P, P], S),
     }
     # the masked FFN calls take (m, E_local, cap_per_expert) where the others take
     # (offsets, E_local, cap_rows): same argument types
@@ -345,13 +350,54 @@ def moe_ffn_workspace_bytes(cap_rows: int, I: int, act_dtype) -> int:
     return int(lib().moe_ffn_workspace_bytes(cap_rows, I, _dtype_code(act_dtype)))
 
 
-def _ffn_shapes(a, w_gate_or_down, gated):
-    E_loc = w_gate_or_down.shape[0]
-    if gated:
-        I, H = w_gate_or_down.shape[1], w_gate_or_down.shape[2]
-    else:
-        H, I = w_gate_or_down.shape[1], w_gate_or_down.shape[2]
-    return E_loc, H, I
+def moe_weight_ld(cols: int, w_dtype) -> int:
+    """Row pitch (elements) of packed weights with rows of ``cols`` elements."""
+    ld = int(lib().moe_weight_ld(int(cols), _dtype_code(w_dtype)))
+    if ld < 0:
+        raise ValueError(f"no packed pitch for cols={cols}, dtype={w_dtype}")
+    return ld
+
+
+def moe_packed_weight_bytes(E_local: int, rows: int, cols: int, w_dtype) -> int:
+    return int(lib().moe_packed_weight_bytes(E_local, rows, cols, _dtype_code(w_dtype)))
+
+
+def moe_pack_weights(w, out=None, stream=None):
+    """w (E_local, rows, cols) -> (E_local, rows, moe_weight_ld(cols)), rows
+    unchanged and the padding zero: the layout the FFN calls read when given
+    weights with the packed pitch (results identical to the dense weights)."""
+    _dev(w, "w", ndim=3)
+    E_loc, rows, cols = w.shape
+    code = _DT[w.dtype]
+    ld = moe_weight_ld(cols, code)
+    if out is None:
+        out = torch.empty((E_loc, rows, ld), dtype=w.dtype, device=w.device)
+    _dev(out, "out", w.dtype)
+    _need(out, "out", shape=(E_loc, rows, ld))
+    _check(lib().moe_pack_weights(_ptr(w), E_loc, rows, cols, code, _ptr(out), _stream(stream)))
+    return out
+
+
+def _w_packed(w, in_dim, act, name):
+    """Layout of weight tensor w (E_local, out, last): False if last is the
+    input dim (dense), True if it is the packed pitch, None when the packed
+    pitch equals the input dim (both layouts are the same)."""
+    ld = moe_weight_ld(in_dim, act)
+    last = w.shape[2]
+    if last == in_dim:
+        return None if ld == in_dim else False
+    if last == ld:
+        return True
+    raise ValueError(f"{name} must have {in_dim} columns (dense) or {ld} (packed), got {last}")
+
+
+def _pack_flag(*layouts):
+    """MOE_W_PACKED if the call's weights are packed; all of one call's
+    weights share one layout."""
+    seen = {x for x in layouts if x is not None}
+    if len(seen) > 1:
+        raise ValueError("the weights of one call must be all packed or all dense")
+    return MOE_W_PACKED if seen == {True} else 0
 
 
 def _rows_arg(rows, cap_per_expert, E_loc, n_rows):
@@ -408,10 +454,11 @@ def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_
     _dev(xd, "xd", ndim=2)
     _dev(w_gate, "w_gate", xd.dtype, 3)
     _dev(w_up, "w_up", xd.dtype, 3)
-    E_loc, H, I = _ffn_shapes(xd, w_gate, True)
+    E_loc, I, H = w_gate.shape[0], w_gate.shape[1], xd.shape[1]
     cap = xd.shape[0]
     third = _rows_arg(offsets, cap_per_expert, E_loc, cap)
     act = _DT[xd.dtype]
+    packed = _pack_flag(_w_packed(w_gate, H, act, "w_gate"))
     if h is None:
         h = torch.empty((cap, I), dtype=xd.dtype, device=xd.device)
     if act == MOE_FP8_E4M3 and h_scales is None:
@@ -421,14 +468,15 @@ def moe_ffn_gate_up(xd, xd_scales, offsets, w_gate, w_up, w_gate_scales=None, w_
     nbH, nbI = -(-H // FP8_BLOCK), -(-I // FP8_BLOCK)
     fp8 = act == MOE_FP8_E4M3
     _check_ffn(xd, xd_scales, offsets, cap_per_expert, E_loc, H, cap, act,
-               w_up=(w_up, (E_loc, I, H)), h=(h, cap * I),
+               w_up=(w_up, tuple(w_gate.shape)), h=(h, cap * I),
                h_scales=(h_scales if fp8 else None, cap * nbI),
                w_gate_scales=(w_gate_scales if fp8 else None, (E_loc, I, nbH)),
                w_up_scales=(w_up_scales if fp8 else None, (E_loc, I, nbH)))
     fn = lib().moe_ffn_gate_up if cap_per_expert is None else lib().moe_ffn_gate_up_masked
     _check(fn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, third, H, I, act,
               _ptr(w_gate), _ptr(w_up), _ptr(w_gate_scales), _ptr(w_up_scales),
-              _w_code(act, w_scales_pow2), _ptr(h), _ptr(h_scales), int(expected_rows), _stream(stream)))
+              _w_code(act, w_scales_pow2) | packed, _ptr(h), _ptr(h_scales), int(expected_rows),
+              _stream(stream)))
     return h, h_scales
 
 
@@ -442,10 +490,11 @@ def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dty
     w_scales_pow2: as in moe_ffn_gate_up (moe_ffn_down_masked)."""
     _dev(h, "h", ndim=2)
     _dev(w_down, "w_down", h.dtype, 3)
-    E_loc, H, I = _ffn_shapes(h, w_down, False)
+    E_loc, H, I = w_down.shape[0], w_down.shape[1], h.shape[1]
     cap = h.shape[0]
     third = _rows_arg(offsets, cap_per_expert, E_loc, cap)
     act = _DT[h.dtype]
+    packed = _pack_flag(_w_packed(w_down, I, act, "w_down"))
     y_dtype = _y_dtype_for(act) if y_dtype is None else y_dtype
     if y is None:
         y = torch.empty((cap, H), dtype=y_dtype, device=h.device)
@@ -454,7 +503,7 @@ def moe_ffn_down(h, h_scales, offsets, w_down, w_down_scales=None, y=None, y_dty
                w_down_scales=(w_down_scales if fp8 else None, (E_loc, H, -(-I // FP8_BLOCK))))
     fn = lib().moe_ffn_down if cap_per_expert is None else lib().moe_ffn_down_masked
     _check(fn(_ptr(h), _ptr(h_scales), _ptr(offsets), E_loc, third, H, I, act,
-              _ptr(w_down), _ptr(w_down_scales), _w_code(act, w_scales_pow2), _ptr(y), _DT[y.dtype],
+              _ptr(w_down), _ptr(w_down_scales), _w_code(act, w_scales_pow2) | packed, _ptr(y), _DT[y.dtype],
               int(expected_rows), _stream(stream)))
     return y
 
@@ -467,10 +516,11 @@ def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=
     _dev(xd, "xd", ndim=2)
     for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _dev(w, n, xd.dtype, 3)
-    E_loc, H, I = _ffn_shapes(xd, w_gate, True)
+    E_loc, I, H = w_gate.shape[0], w_gate.shape[1], xd.shape[1]
     cap = xd.shape[0]
     third = _rows_arg(offsets, cap_per_expert, E_loc, cap)
     act = _DT[xd.dtype]
+    packed = _pack_flag(_w_packed(w_gate, H, act, "w_gate"), _w_packed(w_down, I, act, "w_down"))
     y_dtype = _y_dtype_for(act) if y_dtype is None else y_dtype
     if y is None:
         y = torch.empty((cap, H), dtype=y_dtype, device=xd.device)
@@ -480,14 +530,15 @@ def moe_grouped_ffn(xd, xd_scales, offsets, w_gate, w_up, w_down, w_gate_scales=
     fp8 = act == MOE_FP8_E4M3
     nbH, nbI = -(-H // FP8_BLOCK), -(-I // FP8_BLOCK)
     _check_ffn(xd, xd_scales, offsets, cap_per_expert, E_loc, H, cap, act,
-               w_up=(w_up, (E_loc, I, H)), w_down=(w_down, (E_loc, H, I)), y=(y, cap * H),
+               w_up=(w_up, tuple(w_gate.shape)), w_down=(w_down, (E_loc, H, w_down.shape[2])),
+               y=(y, cap * H),
                w_gate_scales=(w_gate_scales if fp8 else None, (E_loc, I, nbH)),
                w_up_scales=(w_up_scales if fp8 else None, (E_loc, I, nbH)),
                w_down_scales=(w_down_scales if fp8 else None, (E_loc, H, nbI)))
     fn = lib().moe_grouped_ffn if cap_per_expert is None else lib().moe_grouped_ffn_masked
     _check(fn(_ptr(xd), _ptr(xd_scales), _ptr(offsets), E_loc, third, H, I, act,
               _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
-              _ptr(w_up_scales), _ptr(w_down_scales), _w_code(act, w_scales_pow2), _ptr(y),
+              _ptr(w_up_scales), _ptr(w_down_scales), _w_code(act, w_scales_pow2) | packed, _ptr(y),
               _DT[y.dtype], _ptr(ws), ws.numel() * ws.element_size(),
               int(expected_rows), _stream(stream)))
     return y

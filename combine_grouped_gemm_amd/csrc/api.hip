@@ -97,9 +97,10 @@ moe_status_t check_y_dtype(moe_dtype_t act_dt, moe_dtype_t y_dt) {
 moeep::FfnArgs ffn_args(const void* a, const float* a_scales, Rows rows, int E_local,
                         int cap_rows, int Kdim, int N, const void* w0, const void* w1,
                         const float* w0s, const float* w1s, void* out, float* out_scales,
-                        int expected_rows, moe_dtype_t w_dt) {
+                        int expected_rows, moe_dtype_t w_dt, int ldw) {
     moeep::FfnArgs f;
     f.w_scales_pow2 = w_dt == MOE_FP8_E4M3_PO2;
+    f.ldw = ldw;
     f.a = a;
     f.a_scales = a_scales;
     f.offsets = rows.offsets;
@@ -130,6 +131,23 @@ hipError_t run_ffn(const moeep::FfnArgs& f, moe_dtype_t act_dt, bool gated, hipS
 
 size_t elem_size(moe_dtype_t d) { return d == MOE_F32 ? 4 : d == MOE_BF16 ? 2 : 1; }
 
+// Row pitch (elements) of packed weights: whole 128-byte lines, plus one line
+// when the row length is a multiple of 4 KiB (rows exactly 4 KiB apart
+// stream markedly slower than rows one line further apart).
+int packed_ld(int cols, size_t esz) {
+    size_t bytes = ((size_t)cols * esz + 127) / 128 * 128;
+    if (bytes % 4096 == 0) bytes += 128;
+    return (int)(bytes / esz);
+}
+
+// a weight dtype argument: the element type, and whether the rows sit at the packed pitch
+struct WType {
+    moe_dtype_t dt;
+    bool packed;
+};
+WType split_w(moe_dtype_t w_dt) { return WType{w_dt & ~MOE_W_PACKED, (w_dt & MOE_W_PACKED) != 0}; }
+int weight_ld(WType wt, int cols) { return wt.packed ? packed_ld(cols, elem_size(wt.dt)) : cols; }
+
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
 size_t ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt) {
@@ -144,14 +162,15 @@ moe_status_t ffn_gate_up(const void* xd, const float* xd_scales, Rows rows,
                              const void* w_gate, const void* w_up, const float* w_gate_scales,
                              const float* w_up_scales, moe_dtype_t w_dt, void* h, float* h_scales,
                              int expected_rows, hipStream_t stream) {
-    moe_status_t s = check_ffn_common(xd, rows, E_local, cap_rows, H, I, act_dt, w_dt);
+    const WType wt = split_w(w_dt);
+    moe_status_t s = check_ffn_common(xd, rows, E_local, cap_rows, H, I, act_dt, wt.dt);
     if (s != MOE_OK) return s;
     REQUIRE(w_gate && w_up && h, "null weight or h pointer");
     REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(h), "weights and h must be 16-byte aligned");
     if (act_dt == MOE_FP8_E4M3)
         REQUIRE(xd_scales && w_gate_scales && w_up_scales && h_scales, "fp8 needs all scale pointers");
     auto f = ffn_args(xd, xd_scales, rows, E_local, cap_rows, H, I, w_gate, w_up, w_gate_scales,
-                      w_up_scales, h, h_scales, expected_rows, w_dt);
+                      w_up_scales, h, h_scales, expected_rows, wt.dt, weight_ld(wt, H));
     return launched(run_ffn(f, act_dt, true, stream), "ffn gate/up");
 }
 
@@ -159,7 +178,8 @@ moe_status_t ffn_down(const void* h, const float* h_scales, Rows rows, int E_loc
                           int cap_rows, int H, int I, moe_dtype_t act_dt, const void* w_down,
                           const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
                           int expected_rows, hipStream_t stream) {
-    moe_status_t s = check_ffn_common(h, rows, E_local, cap_rows, H, I, act_dt, w_dt);
+    const WType wt = split_w(w_dt);
+    moe_status_t s = check_ffn_common(h, rows, E_local, cap_rows, H, I, act_dt, wt.dt);
     if (s != MOE_OK) return s;
     s = check_y_dtype(act_dt, y_dt);
     if (s != MOE_OK) return s;
@@ -167,7 +187,7 @@ moe_status_t ffn_down(const void* h, const float* h_scales, Rows rows, int E_loc
     REQUIRE(aligned16(w_down) && aligned16(y), "weights and y must be 16-byte aligned");
     if (act_dt == MOE_FP8_E4M3) REQUIRE(h_scales && w_down_scales, "fp8 needs all scale pointers");
     auto f = ffn_args(h, h_scales, rows, E_local, cap_rows, I, H, w_down, nullptr, w_down_scales,
-                      nullptr, y, nullptr, expected_rows, w_dt);
+                      nullptr, y, nullptr, expected_rows, wt.dt, weight_ld(wt, I));
     return launched(run_ffn(f, act_dt, false, stream), "ffn down");
 }
 
@@ -177,7 +197,7 @@ moe_status_t grouped_ffn(const void* xd, const float* xd_scales, Rows rows,
                              const float* w_gate_scales, const float* w_up_scales,
                              const float* w_down_scales, moe_dtype_t w_dt, void* y, moe_dtype_t y_dt,
                              void* ws, size_t ws_bytes, int expected_rows, hipStream_t stream) {
-    moe_status_t s = check_ffn_common(xd, rows, E_local, cap_rows, H, I, act_dt, w_dt);
+    moe_status_t s = check_ffn_common(xd, rows, E_local, cap_rows, H, I, act_dt, split_w(w_dt).dt);
     if (s != MOE_OK) return s;
     s = check_y_dtype(act_dt, y_dt);
     if (s != MOE_OK) return s;
@@ -370,6 +390,44 @@ moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int
 
 size_t moe_ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt) {
     return ffn_workspace_bytes(cap_rows, I, act_dt);
+}
+
+static bool packable_dtype(moe_dtype_t w_dt) {
+    return w_dt == MOE_F32 || w_dt == MOE_BF16 || w_dt == MOE_FP8_E4M3 || w_dt == MOE_FP8_E4M3_PO2;
+}
+
+int moe_weight_ld(int cols, moe_dtype_t w_dt) {
+    if (cols < 1 || cols > (1 << 24) || !packable_dtype(w_dt & ~MOE_W_PACKED)) return -1;
+    return packed_ld(cols, elem_size(w_dt & ~MOE_W_PACKED));
+}
+
+size_t moe_packed_weight_bytes(int E_local, int rows, int cols, moe_dtype_t w_dt) {
+    const int ld = moe_weight_ld(cols, w_dt);
+    if (ld < 0 || E_local < 0 || rows < 0) return 0;
+    return (size_t)E_local * (size_t)rows * (size_t)ld * elem_size(w_dt & ~MOE_W_PACKED);
+}
+
+moe_status_t moe_pack_weights(const void* w, int E_local, int rows, int cols, moe_dtype_t w_dt,
+                              void* w_packed, hipStream_t stream) {
+    const moe_dtype_t dt = w_dt & ~MOE_W_PACKED;
+    if (!packable_dtype(dt)) return fail(MOE_ERR_UNSUPPORTED, "unsupported weight dtype %d", w_dt);
+    REQUIRE(E_local >= 0 && rows >= 0, "E_local and rows must be >= 0");
+    REQUIRE(cols >= 8 && cols % 8 == 0 && cols <= (1 << 24), "cols must be a positive multiple of 8 (got %d)", cols);
+    if ((long long)E_local * rows == 0) {
+        g_last_error[0] = '\0';
+        return MOE_OK;
+    }
+    REQUIRE(w && w_packed, "null weight pointer");
+    REQUIRE(aligned16(w) && aligned16(w_packed), "weights must be 16-byte aligned");
+    const size_t esz = elem_size(dt);
+    const size_t row_bytes = (size_t)cols * esz, ld_bytes = (size_t)packed_ld(cols, esz) * esz;
+    const long long n_rows = (long long)E_local * rows;
+    const char* s0 = static_cast<const char*>(w);
+    const char* d0 = static_cast<const char*>(w_packed);
+    REQUIRE(d0 + (size_t)n_rows * ld_bytes <= s0 || s0 + (size_t)n_rows * row_bytes <= d0,
+            "w and w_packed must not overlap");
+    return launched(moeep::launch_pack_rows(w, n_rows, (int)row_bytes, (int)ld_bytes, w_packed, stream),
+                    "moe_pack_weights");
 }
 
 moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32_t* offsets,

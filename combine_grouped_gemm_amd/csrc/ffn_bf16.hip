@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int wm = wave / WNW, wn = wave % WNW;
-    const int Kdim = p.Kdim, N = p.N, cap = p.cap;
+    const int Kdim = p.Kdim, N = p.N, cap = p.cap, ldw = p.ldw;
 
     build_tile_prefix<NT, BM>(p, s_pre, s_tmp);
     const int n_tiles_n = (N + BNO - 1) / BNO;
@@ -74,8 +74,8 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
 
-        const uint16_t* wg = W0 + (size_t)j * N * Kdim;
-        const uint16_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
+        const uint16_t* wg = W0 + (size_t)j * N * ldw;
+        const uint16_t* wu = GATED ? W1 + (size_t)j * N * ldw : nullptr;
 
         // ---- global -> register staging
         uint4 ra[A_IT], rb[B_IT];
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
                         col = col0 + r;
                         src = wg;
                     }
-                    if (col < N) rb[i] = load_stream16(src + (size_t)col * Kdim + k0 + c * 8);
+                    if (col < N) rb[i] = load_stream16(src + (size_t)col * ldw + k0 + c * 8);
                 }
             }
         };
@@ -221,7 +221,7 @@ hipError_t launch_wide(const FfnArgs& a, hipStream_t stream) {
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, bool gated, hipStream_t stream) {
     // the wide kernels address one expert's weight matrix with 32-bit offsets
-    const bool wide_ok = (unsigned long long)a.N * a.Kdim * 2 < (1ull << 32);
+    const bool wide_ok = (unsigned long long)a.N * a.ldw * 2 < (1ull << 32);
     if (wide_ok && a.rows_hint >= 192)   // ~256-row experts: one 320-row tile holds nearly all
         return gated ? launch_wide<320, true>(a, stream) : launch_wide<320, false>(a, stream);
     if (wide_ok && a.rows_hint >= 64)

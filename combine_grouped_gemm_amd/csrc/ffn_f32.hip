@@ -32,12 +32,12 @@ __global__ __launch_bounds__(kThreads) void grouped_ffn_f32_kernel(FfnArgs p) {
     const int j = blockIdx.x;
     const int col0 = blockIdx.y * kCols;
     const int tid = threadIdx.x, c = tid % kCols, g = tid / kCols;
-    const int N = p.N, Kdim = p.Kdim;
+    const int N = p.N, Kdim = p.Kdim, ldw = p.ldw;
     int r0, r1;
     expert_rows(p, j, r0, r1);
     const float* A = static_cast<const float*>(p.a);
-    const float* W0 = static_cast<const float*>(p.w0) + (size_t)j * N * Kdim;
-    const float* W1 = GATED ? static_cast<const float*>(p.w1) + (size_t)j * N * Kdim : nullptr;
+    const float* W0 = static_cast<const float*>(p.w0) + (size_t)j * N * ldw;
+    const float* W1 = GATED ? static_cast<const float*>(p.w1) + (size_t)j * N * ldw : nullptr;
     float* Out = static_cast<float*>(p.out);
 
     for (int rb = r0; rb < r1; rb += kRowBlock) {
@@ -52,8 +52,8 @@ __global__ __launch_bounds__(kThreads) void grouped_ffn_f32_kernel(FfnArgs p) {
                 const int col = col0 + cc;
                 float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
                 if (col < N) {
-                    v0 = *reinterpret_cast<const float4*>(W0 + (size_t)col * Kdim + k0 + k4);
-                    if (GATED) v1 = *reinterpret_cast<const float4*>(W1 + (size_t)col * Kdim + k0 + k4);
+                    v0 = *reinterpret_cast<const float4*>(W0 + (size_t)col * ldw + k0 + k4);
+                    if (GATED) v1 = *reinterpret_cast<const float4*>(W1 + (size_t)col * ldw + k0 + k4);
                 }
                 sW0[cc][k4] = v0.x; sW0[cc][k4 + 1] = v0.y; sW0[cc][k4 + 2] = v0.z; sW0[cc][k4 + 3] = v0.w;
                 if (GATED) {

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int wm = wave / WNW, wn = wave % WNW;
-    const int Kdim = p.Kdim, N = p.N, cap = p.cap;
+    const int Kdim = p.Kdim, N = p.N, cap = p.cap, ldw = p.ldw;
     const int nbK = (Kdim + BKB - 1) / BKB;
     const int nbN = (N + 127) / 128;
 
@@ -77,8 +77,8 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
         const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
-        const uint8_t* wg = W0 + (size_t)j * N * Kdim;
-        const uint8_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
+        const uint8_t* wg = W0 + (size_t)j * N * ldw;
+        const uint8_t* wu = GATED ? W1 + (size_t)j * N * ldw : nullptr;
         const float* wgs = p.w0_scales + (size_t)j * N * nbK;
         const float* wus = GATED ? p.w1_scales + (size_t)j * N * nbK : nullptr;
 
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_fp8_kernel(FfnArg
                         src = wg;
                     }
                     rb[i] = (col < N && k0 + c * 16 < Kdim)
-                                ? *reinterpret_cast<const uint4*>(src + (size_t)col * Kdim + k0 + c * 16)
+                                ? *reinterpret_cast<const uint4*>(src + (size_t)col * ldw + k0 + c * 16)
                                 : make_uint4(0, 0, 0, 0);
                 }
             }
@@ -342,7 +342,7 @@ hipError_t launch_ffn_fp8(const FfnArgs& a, bool gated, hipStream_t stream) {
     // expert's weight matrix with 32-bit offsets
     const int nbK = (a.Kdim + 127) / 128;
     const bool wide_ok = nbK <= widefp8::kMaxKBlocks &&
-                         (unsigned long long)a.N * a.Kdim < (1ull << 32);
+                         (unsigned long long)a.N * a.ldw < (1ull << 32);
     if (wide_ok && a.rows_hint >= 48) {
         if (a.w_scales_pow2)
             return gated ? launch_wide<true, true>(a, stream) : launch_wide<false, true>(a, stream);

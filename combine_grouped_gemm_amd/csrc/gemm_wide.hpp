@@ -148,6 +148,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: keeps LDS bases scalar
     const int wm = wave / WNW, wn = wave % WNW;
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
+    const int ldw = p.ldw;                          // weight row pitch (elements)
     const int nk = Kdim / BK;
 
     // largest experts' tiles first; the first row stage is free scratch until the first load
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
         const TileCoord tc = decode_tile<BM>(tau, n_tiles_n, s_pre, p, s_ord);
         const int j = tc.j, row0 = tc.row0, nvalid = tc.nvalid;
         const int col0 = tc.nt * BNO;
-        const uint16_t* wg = W0 + (size_t)j * N * Kdim;
-        const uint16_t* wu = GATED ? W1 + (size_t)j * N * Kdim : nullptr;
+        const uint16_t* wg = W0 + (size_t)j * N * ldw;
+        const uint16_t* wu = GATED ? W1 + (size_t)j * N * ldw : nullptr;
 
         // Operands come in by buffer loads straight into LDS: a scalar resource
         // per operand (base, byte extent) plus a 32-bit per-lane offset and the
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
         // the tile.
         const char* abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
         const uint32_t a_bytes = (uint32_t)nvalid * (uint32_t)(Kdim * 2);
-        const uint32_t w_bytes = (uint32_t)N * (uint32_t)(Kdim * 2);
+        const uint32_t w_bytes = (uint32_t)N * (uint32_t)(ldw * 2);
         uint32_t off[LPS];
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
             const int r = (is_a ? i * NW : (i - A_ITERS) * NW) * 8 + wave * 8 + lane / 8;
             const uint32_t c16 = (uint32_t)swz(r, lane % 8) * 16;   // logical chunk this lane fetches
             const int rr = (!is_a && GATED && r >= BN / 2) ? r - BN / 2 : r;
-            off[i] = (uint32_t)(is_a ? r : col0 + rr) * (uint32_t)(Kdim * 2) + c16;
+            off[i] = (is_a ? (uint32_t)r * (uint32_t)(Kdim * 2) : (uint32_t)(col0 + rr) * (uint32_t)(ldw * 2)) + c16;
         }
         // direct load i of a stage; `live` false (the step after the last) reads
         // nothing, so every step issues the same LPS loads without a branch

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wave / WNW, wn = wave % WNW;
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
+    const int ldw = p.ldw;                          // weight row pitch (bytes = elements)
     const int nk = (Kdim + ROWB - 1) / ROWB;        // k-steps = scale blocks (<= kMaxKBlocks)
     const bool k_tail = nk * ROWB != Kdim;          // last block holds 64 bytes
     const int nbN = (N + 127) / 128;
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     // next tile's scales and first k-step are issued as soon as every wave has
     // finished the current tile's k-loop, so their latency hides behind the
     // current tile's epilogue (which then works in the second stage's buffers).
-    const bool w_lines = Kdim % 128 == 0;
+    const bool w_lines = ldw % 128 == 0;
     const char* abase = nullptr;
     const char* gbase = nullptr;
     const char* ubase = nullptr;
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             lds_dma4(bsrc + (col < N && k < nk ? (size_t)col * nk + k : 0), s_bs + q * kWave);
         }
         abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
-        gbase = reinterpret_cast<const char*>(W0 + (size_t)j * N * Kdim);
-        ubase = GATED ? reinterpret_cast<const char*>(W1 + (size_t)j * N * Kdim) : nullptr;
+        gbase = reinterpret_cast<const char*>(W0 + (size_t)j * N * ldw);
+        ubase = GATED ? reinterpret_cast<const char*>(W1 + (size_t)j * N * ldw) : nullptr;
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
             const int q = i * NW + wave;                 // wave-uniform
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 const int r = (q - A_BLOCKS) * 8 + lane / 8;
                 const int rr = (GATED && r >= BN / 2) ? r - BN / 2 : r;
                 const int col = col0 + rr;
-                off[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)Kdim + c16;
+                off[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)ldw + c16;
             }
         }
         return tc;

@@ -58,6 +58,7 @@ struct FfnArgs {
     const int32_t* m_counts;  // masked layout: (E_loc) valid rows of expert j, in [j*cap_e, ...)
     int cap_e;                // masked layout: rows per expert block (cap = E_loc * cap_e)
     int E_loc, cap, Kdim, N;  // N = output columns (I for gate/up, H for down)
+    int ldw;                  // weight row pitch in elements (Kdim, or the packed pitch)
     const void* w0;           // gate or down (E_loc, N, Kdim)
     const void* w1;           // up (gate/up only)
     const float* w0_scales;   // fp8 only: (E_loc, N, ceil(Kdim/128))
@@ -73,5 +74,10 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, bool gated, hipStream_t stream);  /
 hipError_t launch_ffn_fp8(const FfnArgs& a, bool gated, hipStream_t stream);   // ffn_fp8.hip
 
 int device_cu_count();   // api.hip: compute units of the current device (cached)
+
+// pack.hip: rows of row_bytes bytes (a multiple of 4) copied to a pitch of
+// ld_bytes (a multiple of 128, >= row_bytes), the padding zeroed
+hipError_t launch_pack_rows(const void* src, long long n_rows, int row_bytes, int ld_bytes, void* dst,
+                            hipStream_t stream);
 
 }  // namespace moeep

@@ -272,7 +272,8 @@ moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int
  * activation block scales of the fp8 path (xd_scales from moe_dispatch,
  * h_scales) are always powers of two; FP8_E4M3_PO2 declares that the
  * weight scales are too, which lets the row-rich kernels apply every scale
- * in the matrix cores (same results up to fp32 rounding order).
+ * in the matrix cores (same results up to fp32 rounding order).  Any w_dt
+ * may carry MOE_W_PACKED: weights packed by moe_pack_weights (below).
  *
  * moe_ffn_gate_up computes h; moe_ffn_down computes y from h;
  * moe_grouped_ffn runs both with h (and h_scales) carved from `ws`, which
@@ -284,6 +285,39 @@ moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int
  * never changes results.  expected_rows <= 0 means cap_rows / E_local.
  */
 size_t moe_ffn_workspace_bytes(int cap_rows, int I, moe_dtype_t act_dt);
+
+/*
+ * Packed expert weights: a one-time layout transform of this library, not a
+ * step of the method (the pages leave the weights' memory layout open).  The
+ * FFN kernels stream every weight row along its input dimension in 128-byte
+ * steps; a row whose length is not a whole number of 128-byte lines makes
+ * every step straddle two lines, and rows exactly a multiple of 4 KiB apart
+ * stream markedly slower than rows one line further apart.
+ *
+ * moe_weight_ld(cols, w_dt): the packed row pitch in elements for rows of
+ *   `cols` elements of w_dt -- the row length rounded up to whole 128-byte
+ *   lines, plus one line when that is a multiple of 4 KiB.  -1 if cols is
+ *   outside [1, 2^24] or w_dt is not a weight dtype.
+ * moe_packed_weight_bytes: E_local * rows * ld elements, in bytes (0 on
+ *   invalid arguments).
+ * moe_pack_weights: w (E_local, rows, cols) of w_dt, row-major and
+ *   contiguous, is written to w_packed (E_local, rows, ld): each row
+ *   unchanged, elements [cols, ld) zero.  cols must be a positive multiple
+ *   of 8; both pointers 16-byte aligned, caller-owned, not overlapping.
+ *   Asynchronous on `stream`; E_local * rows == 0 is a no-op.
+ *
+ * An FFN call whose w_dt carries the flag MOE_W_PACKED (e.g. MOE_BF16 |
+ * MOE_W_PACKED) reads every weight matrix it takes at the packed pitch:
+ * w_gate, w_up (E_local, I, moe_weight_ld(H)), w_down (E_local, H,
+ * moe_weight_ld(I)).  Results are identical to the call on the unpacked
+ * weights; fp8 weight scales are never packed.
+ */
+#define MOE_W_PACKED 0x100
+int moe_weight_ld(int cols, moe_dtype_t w_dt);
+size_t moe_packed_weight_bytes(int E_local, int rows, int cols, moe_dtype_t w_dt);
+moe_status_t moe_pack_weights(const void* w, int E_local, int rows, int cols, moe_dtype_t w_dt,
+                              void* w_packed, hipStream_t stream);
+
 moe_status_t moe_ffn_gate_up(const void* xd, const float* xd_scales, const int32_t* offsets,
                              int E_local, int cap_rows, int H, int I, moe_dtype_t act_dt,
                              const void* w_gate, const void* w_up,

@@ -13,7 +13,7 @@ HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 def declared():
     text = open(HDR).read()
-    return re.findall(r"^\s*(?:moe_status_t|size_t|const char\*)\s+(moe_\w+)\(", text, re.M)
+    return re.findall(r"^\s*(?:moe_status_t|size_t|int|const char\*)\s+(moe_\w+)\(", text, re.M)
 
 
 def test_exports_every_declared_symbol():
@@ -179,3 +179,42 @@ def test_layout_noalloc_rejects_before_any_hip_call():
     assert L.moe_layout_noalloc(p, 4, 2, 8, 0, 8, None, p, p, p, 8, None) == m.MOE_ERR_INVALID_ARG
     # the prefill batch (T = 8192, K = 8, E = 256) fits
     assert L.moe_layout_workspace_bytes(8192, 8, 256) <= limit
+
+
+# (cols, dtype code, packed pitch in elements): whole 128-byte lines, one more
+# line when the row is a multiple of 4 KiB
+PITCHES = [(2048, m.MOE_BF16, 2112), (7168, m.MOE_BF16, 7168), (2880, m.MOE_FP8_E4M3, 2944),
+           (2880, m.MOE_FP8_E4M3_PO2, 2944), (4096, m.MOE_FP8_E4M3, 4224), (128, m.MOE_F32, 128),
+           (1024, m.MOE_F32, 1056), (256, m.MOE_F32, 256), (8, m.MOE_BF16, 64),
+           (2048, m.MOE_BF16 | m.MOE_W_PACKED, 2112)]
+
+
+@pytest.mark.parametrize("cols,dt,ld", PITCHES)
+def test_weight_ld(cols, dt, ld):
+    L = m.lib()
+    assert L.moe_weight_ld(cols, dt) == ld
+    esz = {m.MOE_F32: 4, m.MOE_BF16: 2}.get(dt & ~m.MOE_W_PACKED, 1)
+    assert ld * esz % 128 == 0 and ld >= cols and (ld * esz) % 4096 != 0
+    assert L.moe_packed_weight_bytes(3, 5, cols, dt) == 3 * 5 * ld * esz
+
+
+def test_weight_ld_rejects():
+    L = m.lib()
+    assert L.moe_weight_ld(0, m.MOE_BF16) == -1
+    assert L.moe_weight_ld(64, 7) == -1
+    assert L.moe_packed_weight_bytes(2, 2, 64, 7) == 0
+
+
+def test_pack_weights_rejects_before_any_hip_call():
+    L = m.lib()
+    p, q = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 30)    # never dereferenced
+    assert L.moe_pack_weights(p, 2, 4, 64, 7, q, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(p, 2, 4, 60, m.MOE_BF16, q, None) == m.MOE_ERR_INVALID_ARG
+    assert "multiple of 8" in L.moe_last_error().decode()
+    assert L.moe_pack_weights(None, 2, 4, 64, m.MOE_BF16, q, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(ctypes.c_void_p((1 << 20) + 8), 2, 4, 64, m.MOE_BF16, q, None) == 1
+    assert "16-byte" in L.moe_last_error().decode()
+    # 8 rows of 128 bytes packed to 8 rows of 128: [p, p + 1 KiB) and [p + 512, ...) overlap
+    assert L.moe_pack_weights(p, 2, 4, 64, m.MOE_BF16, ctypes.c_void_p((1 << 20) + 512), None) == 1
+    assert "overlap" in L.moe_last_error().decode()
+    assert L.moe_pack_weights(None, 0, 4, 64, m.MOE_BF16, None, None) == m.MOE_OK
