@@ -174,8 +174,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
         return tc;
     };
     // Weight rows are streamed with the non-temporal hint only when they start
-    // on 128-byte lines: otherwise a k-step's 128 bytes straddle two lines and
-    // the next k-step re-reads the second one, which must still be in L2.
+    // on 128-byte lines (a row pitch that is a multiple of 128, as packed
+    // weights have): otherwise a k-step's 128 bytes straddle two lines and the
+    // next k-step re-reads the second one, which must still be in L2.
     auto issue_p = [&](auto I, int kstep, auto WPOL) {
         const uint32_t kb = (uint32_t)kstep * ROWB;
         // in a 64-byte tail block, chunks 4..7 come from the zero block

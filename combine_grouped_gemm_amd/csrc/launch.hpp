@@ -59,7 +59,7 @@ struct FfnArgs {
     int cap_e;                // masked layout: rows per expert block (cap = E_loc * cap_e)
     int E_loc, cap, Kdim, N;  // N = output columns (I for gate/up, H for down)
     int ldw;                  // weight row pitch in elements (Kdim, or the packed pitch)
-    const void* w0;           // gate or down (E_loc, N, Kdim)
+    const void* w0;           // gate or down (E_loc, N, ldw): rows of Kdim at pitch ldw
     const void* w1;           // up (gate/up only)
     const float* w0_scales;   // fp8 only: (E_loc, N, ceil(Kdim/128))
     const float* w1_scales;
