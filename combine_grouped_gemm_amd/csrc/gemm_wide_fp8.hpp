@@ -14,8 +14,12 @@
 // so each weight tile is streamed from HBM once.
 //
 // Scales: the tile's row scales and weight-column scales for every k-block
-// are copied to LDS once per tile with 4-byte direct loads over contiguous
-// runs, row-major with a fixed row stride.  Row (activation) scales are powers of two, so the scaled MFMA
+// are copied to LDS once per tile, row-major with a fixed row stride of 23
+// blocks.  With exactly 23 blocks (K in (2816, 2944]) the stride equals the
+// global one, so the tile's row scales and each 128-row weight half's scales
+// are one contiguous run each, copied with 16-byte loads (≈ 6 per wave
+// instead of ≈ 20 four-byte ones); other K use 4-byte loads over the flat
+// index.  Row (activation) scales are powers of two, so the scaled MFMA
 // v_mfma_scale_f32_16x16x128_f8f6f4 applies them itself, exactly, as E8M0
 // bytes (lane l gives the scale of the row it feeds, l % 16, for its 32-byte
 // slice l / 16 of the block).  With arbitrary fp32 weight scales the block
@@ -52,6 +56,24 @@ __device__ __forceinline__ void lds_dma4(const void* g, void* lds_wave_base) {
 #endif
 }
 
+// Copies the contiguous run [run, run + count) of a scale array ending at
+// `end` into LDS at lds + sh, sh = the run's float offset from the 16-byte
+// boundary at or below it (returned; uniform): 16-byte direct buffer loads
+// spread over the waves, lanes past the run's last piece masked off, pieces
+// past `end` landing zeros.  lds must hold count + 3 floats.
+template <int NW>
+__device__ __forceinline__ int stage_scale_run(const float* run, const float* end, int count, float* lds,
+                                               int wave, int lane) {
+    const int sh = __builtin_amdgcn_readfirstlane((int)((reinterpret_cast<uintptr_t>(run) & 15u) >> 2));
+    const float* al = run - sh;
+    const wide::rsrc_t r = wide::make_rsrc(al, (uint32_t)((end - al) * 4));
+    const int n16 = (sh + count + 3) >> 2;
+    for (int q = wave; q * kWave < n16; q += NW)
+        if (q * kWave + lane < n16)
+            wide::lds_buf16<0>(r, lds + q * kWave * 4, (uint32_t)(q * kWave + lane) * 16u, 0);
+    return sh;
+}
+
 // Waves laid out WMW (rows) x WNW (weight rows); a wave owns the interleaved
 // 16-row fragments {wm, wm + WMW, ...} and BN / WNW weight rows.
 template <int BM, int BN, int WMW, int WNW, bool GATED, bool PO2W>
@@ -68,15 +90,17 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     static_assert(BM % (16 * WMW) == 0 && BN % (16 * WNW) == 0 && (!GATED || (FN % 2 == 0 && BNO == 128)),
                   "tile shape");
     static_assert(BLOCKS % NW == 0, "every wave issues LPS loads per stage");
-    static_assert(BM * SK % kWave == 0 && BN * SK % kWave == 0, "scale staging by 64-lane loads");
+    static_assert(BM * SK % kWave == 0 && BN * SK % kWave == 0 && BN / 2 * SK % kWave == 0,
+                  "scale staging by 64-lane loads");
 
     __shared__ uint4 sa0[BM * CPR];
     __shared__ uint4 sb0[BN * CPR];
     __shared__ uint4 sa1[BM * CPR];
     __shared__ uint4 sb1[BN * CPR];
-    // scales, row-major with row stride SK: [tile row][k-block], [tile weight row][k-block]
-    __shared__ float s_as[BM * SK];
-    __shared__ float s_bs[BN * SK];
+    // scales, row-major with row stride SK: [tile row][k-block], [tile weight row][k-block],
+    // each table starting a_sh / b_sh[half] floats into its region (room for the shift)
+    __shared__ float s_as[BM * SK + 4];
+    __shared__ float s_bs[BN * SK + 8];
     __shared__ int s_pre[kMaxExperts + 1];
     __shared__ uint16_t s_ord[kMaxExperts];          // experts, most rows first
     static_assert(sizeof(sa0) >= kMaxExperts * sizeof(int), "row counts fit in the first row stage");
@@ -124,6 +148,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     const char* gbase = nullptr;
     const char* ubase = nullptr;
     uint32_t off[LPS];
+    int a_sh = 0, b_sh0 = 0, b_sh1 = 4;
 
     // decode tile t, copy its scales to LDS and set the load state.  Scales go
     // row-major with a fixed row stride of SK = kMaxKBlocks floats ([tile
@@ -143,16 +168,37 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
         const float* wgs = p.w0_scales + (size_t)j * N * nk;
         const float* wus = GATED ? p.w1_scales + (size_t)j * N * nk : nullptr;
         const float* asrc = p.a_scales + (size_t)row0 * nk;
-        for (int q = wave; q < BM * SK / kWave; q += NW) {
-            const int e = q * kWave + lane, r = e / SK, k = e - r * SK;
-            lds_dma4(asrc + (r < nvalid && k < nk ? r * nk + k : 0), s_as + q * kWave);
-        }
-        for (int q = wave; q < BN * SK / kWave; q += NW) {
-            const int e = q * kWave + lane, c = e / SK, k = e - c * SK;      // tile weight row c
-            const bool up = GATED && c >= BN / 2;
-            const int col = col0 + (up ? c - BN / 2 : c);
-            const float* bsrc = up ? wus : wgs;
-            lds_dma4(bsrc + (col < N && k < nk ? (size_t)col * nk + k : 0), s_bs + q * kWave);
+        if (nk == SK) {
+            // K = 23 blocks: a run of rows' scales is the table itself, so each
+            // table (the tile's rows; each 128-row weight half) is one
+            // contiguous run, copied with 16-byte loads
+            a_sh = stage_scale_run<NW>(asrc, p.a_scales + (size_t)cap * nk, nvalid * nk, s_as, wave, lane);
+            const int c1 = GATED ? col0 : col0 + BN / 2;
+            const int n0 = min(BN / 2, N - col0), n1 = min(BN / 2, N - c1);
+            b_sh0 = stage_scale_run<NW>(wgs + (size_t)col0 * nk, wgs + (size_t)N * nk, n0 * nk, s_bs, wave, lane);
+            if (n1 > 0) {
+                const float* h1 = GATED ? wus : wgs;
+                b_sh1 = 4 + stage_scale_run<NW>(h1 + (size_t)c1 * nk, h1 + (size_t)N * nk, n1 * nk,
+                                                s_bs + BN / 2 * SK + 4, wave, lane);
+            }
+        } else {
+            a_sh = 0;
+            b_sh0 = 0;
+            b_sh1 = 4;
+            for (int q = wave; q < BM * SK / kWave; q += NW) {
+                const int e = q * kWave + lane, r = e / SK, k = e - r * SK;
+                lds_dma4(asrc + (r < nvalid && k < nk ? r * nk + k : 0), s_as + q * kWave);
+            }
+            for (int q = wave; q < BN * SK / kWave; q += NW) {
+                const int e = q * kWave + lane, c = e / SK, k = e - c * SK;      // tile weight row c
+                const bool up = GATED && c >= BN / 2;
+                const int col = col0 + (up ? c - BN / 2 : c);
+                const float* bsrc = up ? wus : wgs;
+                // the second half's table starts 4 floats further on (a wave's 64
+                // entries never straddle the halves, so the LDS base stays uniform)
+                lds_dma4(bsrc + (col < N && k < nk ? (size_t)col * nk + k : 0),
+                         s_bs + q * kWave + (q * kWave >= BN / 2 * SK ? 4 : 0));
+            }
         }
         abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
         gbase = reinterpret_cast<const char*>(W0 + (size_t)j * N * ldw);
@@ -245,7 +291,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 const uint4 t1 = *reinterpret_cast<const uint4*>(bb + r * ROWB + wide::swz(r, c0 + 1) * 16);
                 bfr[f] = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
                                (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-                bsc[f] = s_bs[r * SK + kstep];
+                bsc[f] = s_bs[(r < BN / 2 ? b_sh0 : b_sh1) + r * SK + kstep];
             }
             int sb8[FN];        // weight-row scales as E8M0 bytes (power-of-two weight scales)
 #pragma unroll
@@ -261,7 +307,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                                             (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
                     // the row scale (a power of two) of the A row this lane
                     // feeds, as an E8M0 byte: the matrix core applies it
-                    const int sa8 = e8m0_of_pow2(s_as[r * SK + kstep]);
+                    const int sa8 = e8m0_of_pow2(s_as[a_sh + r * SK + kstep]);
                     if constexpr (PO2W) {
                         // both scales in the matrix core: accumulate in place
 #pragma unroll
