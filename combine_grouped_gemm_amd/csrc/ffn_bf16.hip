@@ -227,8 +227,10 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, bool gated, hipStream_t stream) {
     if (wide_ok && a.rows_hint >= 64)
         return gated ? launch_wide<256, true>(a, stream) : launch_wide<256, false>(a, stream);
     if (a.rows_hint < 24) {
-        return gated ? launch_cfg<16, 128, 1, 4, true>(a, stream)
-                     : launch_cfg<16, 128, 1, 4, false>(a, stream);
+        // decode-sized experts: 16-row tiles of two waves (more workgroups per
+        // CU than four-wave ones: DeepSeek decode gate/up -1.6%, down -1%)
+        return gated ? launch_cfg<16, 128, 1, 2, true>(a, stream)
+                     : launch_cfg<16, 128, 1, 2, false>(a, stream);
     }
     return gated ? launch_cfg<128, 128, 2, 2, true>(a, stream)
                  : launch_cfg<128, 128, 2, 2, false>(a, stream);
