@@ -294,5 +294,16 @@ def test_full_size_sampled(name):
                 acc += np.float64(np.float32(gates[t, k])) * yk
         ref = oracle.numerics.round_act(acc, cfg.out_dtype)
         assert_close(to_np(layer.out[int(t)]), ref, cfg.act_dtype, f"out[{t}]")
-    del case, layer
+    # the bench feeds the weights packed to the padded row pitch: at full size
+    # that layer gives the same bits as the one checked above
+    import combine_grouped_gemm_amd as m
+    y0, out0 = layer.y[:R].clone(), layer.out.clone()
+    pk = dict(case.wdict)
+    for k in ("gate", "up", "down"):
+        pk[k] = m.moe_pack_weights(case.wdict[k])
+    layer.forward(case.x_dev, case.logits_dev, pk)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.y[:R].contiguous().view(torch.uint8), y0.contiguous().view(torch.uint8)), "y (packed)"
+    assert torch.equal(layer.out.contiguous().view(torch.uint8), out0.contiguous().view(torch.uint8)), "out (packed)"
+    del case, layer, pk, y0, out0
     _free()
