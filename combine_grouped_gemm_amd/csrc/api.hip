@@ -77,8 +77,10 @@ moe_status_t check_ffn_common(const void* a, Rows rows, int E_local, int cap_row
     REQUIRE(a && (rows.offsets || rows.m), "null activation or row-count pointer");
     REQUIRE(E_local >= 1 && E_local <= 1024, "E_local must be in [1, 1024] (got %d)", E_local);
     REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
-    REQUIRE(H >= 64 && H % 64 == 0 && I >= 64 && I % 64 == 0,
-            "H and I must be positive multiples of 64 (got H=%d, I=%d)", H, I);
+    // rows move in 16-byte pieces: 8 elements (bf16, fp32), 16 for fp8
+    const int q = act_dt == MOE_FP8_E4M3 ? 16 : 8;
+    REQUIRE(H >= q && H % q == 0 && I >= q && I % q == 0,
+            "H and I must be positive multiples of %d for this dtype (got H=%d, I=%d)", q, H, I);
     REQUIRE((long long)cap_rows * (H > I ? H : I) <= 0x7fffffffLL * 4LL, "cap_rows * H too large");
     REQUIRE(aligned16(a), "activation pointer must be 16-byte aligned");
     const bool ok = (act_dt == MOE_F32 && w_dt == MOE_F32) || (act_dt == MOE_BF16 && w_dt == MOE_BF16) ||
@@ -357,7 +359,9 @@ moe_status_t moe_dispatch(const void* const* seg_x, const int32_t* seg_rows, int
     REQUIRE(n_seg >= 1 && n_seg <= MOE_MAX_SEGMENTS, "n_seg must be in [1, %d]", MOE_MAX_SEGMENTS);
     REQUIRE(seg_x && seg_rows, "null segment tables");
     REQUIRE(K >= 1 && K <= 1024, "K must be in [1, 1024]");
-    REQUIRE(H >= 64 && H % 64 == 0, "H must be a positive multiple of 64 (got %d)", H);
+    // 16-byte pieces: 8 elements; fp8 rows feed the fp8 GEMMs, which need 16
+    const int q = xd_dt == MOE_FP8_E4M3 ? 16 : 8;
+    REQUIRE(H >= q && H % q == 0, "H must be a positive multiple of %d for this dtype (got %d)", q, H);
     REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
     int kind;
     if (x_dt == MOE_F32 && xd_dt == MOE_F32) kind = 0;
@@ -506,7 +510,7 @@ moe_status_t moe_combine(const void* y, moe_dtype_t y_dt, int cap_rows, const in
                          hipStream_t stream) {
     REQUIRE(B >= 0 && K >= 1 && K <= 1024, "need B >= 0 and 1 <= K <= 1024");
     REQUIRE((long long)B * K <= 0x7fffffffLL, "B*K must fit in int32");
-    REQUIRE(H >= 64 && H % 64 == 0, "H must be a positive multiple of 64 (got %d)", H);
+    REQUIRE(H >= 8 && H % 8 == 0, "H must be a positive multiple of 8 (got %d)", H);
     REQUIRE(cap_rows >= 0, "cap_rows must be >= 0");
     int kind;
     if (y_dt == MOE_F32 && out_dt == MOE_F32) kind = 0;

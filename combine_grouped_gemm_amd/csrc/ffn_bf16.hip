@@ -88,8 +88,11 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
             for (int i = 0; i < A_IT; ++i) {
                 const int q = tid + i * NT;
                 const int r = q >> 3, c = q & 7;
+                // chunks past K (a partial last step) are zero
                 if (q < BM * 8 && r < nvalid)
-                    ra[i] = *reinterpret_cast<const uint4*>(A + (size_t)(row0 + r) * Kdim + k0 + c * 8);
+                    ra[i] = k0 + c * 8 < Kdim
+                                ? *reinterpret_cast<const uint4*>(A + (size_t)(row0 + r) * Kdim + k0 + c * 8)
+                                : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < B_IT; ++i) {
@@ -106,7 +109,9 @@ __global__ __launch_bounds__(64 * WMW * WNW) void grouped_gemm_bf16_kernel(FfnAr
                         col = col0 + r;
                         src = wg;
                     }
-                    if (col < N) rb[i] = load_stream16(src + (size_t)col * ldw + k0 + c * 8);
+                    if (col < N)
+                        rb[i] = k0 + c * 8 < Kdim ? load_stream16(src + (size_t)col * ldw + k0 + c * 8)
+                                                  : make_uint4(0, 0, 0, 0);
                 }
             }
         };
@@ -221,7 +226,10 @@ hipError_t launch_wide(const FfnArgs& a, hipStream_t stream) {
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, bool gated, hipStream_t stream) {
     // the wide kernels address one expert's weight matrix with 32-bit offsets
-    const bool wide_ok = (unsigned long long)a.N * a.ldw * 2 < (1ull << 32);
+    // and keep every resource extent (plus the k-step offset) below 2^31, so
+    // that an out-of-range lane offset exists
+    const bool wide_ok = (unsigned long long)a.N * a.ldw * 2 < (1ull << 31) &&
+                         (unsigned long long)320 * (a.Kdim + 64) * 2 < (1ull << 31);
     if (wide_ok && a.rows_hint >= 192)   // ~256-row experts: one 320-row tile holds nearly all
         return gated ? launch_wide<320, true>(a, stream) : launch_wide<320, false>(a, stream);
     if (wide_ok && a.rows_hint >= 64)

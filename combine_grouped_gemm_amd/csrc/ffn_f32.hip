@@ -8,7 +8,8 @@
 // coalesced 16-byte loads; thread (c, g) then owns column c and the rows
 // g, g + 4, ... of the row block and accumulates in ascending k.  Same
 // semantics as the MFMA kernels (fp32 accumulation, h and y stored as fp32).
-// The contraction dimension is a multiple of 64 (checked by the C ABI).
+// The contraction dimension is a multiple of 8 (checked by the C ABI); the
+// 16-byte chunks past it in the last k-chunk are read as zero.
 #include "grouped_tiles.hpp"
 
 namespace moeep {
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void grouped_ffn_f32_kernel(FfnArgs p) {
                 const int cc = i / (kChunk / 4), k4 = (i % (kChunk / 4)) * 4;
                 const int col = col0 + cc;
                 float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-                if (col < N) {
+                if (col < N && k0 + k4 < Kdim) {      // chunks past K (a partial last chunk) are zero
                     v0 = *reinterpret_cast<const float4*>(W0 + (size_t)col * ldw + k0 + k4);
                     if (GATED) v1 = *reinterpret_cast<const float4*>(W1 + (size_t)col * ldw + k0 + k4);
                 }
@@ -64,8 +65,9 @@ __global__ __launch_bounds__(kThreads) void grouped_ffn_f32_kernel(FfnArgs p) {
             for (int i = tid; i < kRowBlock * kChunk / 4; i += kThreads) {
                 const int rr = i / (kChunk / 4), k4 = (i % (kChunk / 4)) * 4;
                 const int r = rb + rr;
-                const float4 v = r < r1 ? *reinterpret_cast<const float4*>(A + (size_t)r * Kdim + k0 + k4)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 v = r < r1 && k0 + k4 < Kdim
+                                     ? *reinterpret_cast<const float4*>(A + (size_t)r * Kdim + k0 + k4)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
                 *reinterpret_cast<float4*>(&sA[rr][k4]) = v;
             }
             __syncthreads();

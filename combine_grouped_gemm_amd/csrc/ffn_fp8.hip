@@ -12,8 +12,8 @@
 // e4m3) produces the unscaled block product from a zero accumulator, which
 // is folded into the fp32 accumulator as acc += partial * sa[row] * sb[col].
 // Lane l feeds row (l % 16) with bytes [32*(l/16), 32*(l/16)+32) of the
-// block for both operands.  A 64-wide tail block (K = 2880) is zero-filled
-// on both operands.
+// block for both operands.  A partial tail block (K = 2880 leaves 64 of
+// 128; K is a multiple of 16) is zero-filled on both operands.
 //
 // gate/up writes h as fp8: each tile covers exactly one 128-column block of
 // h per row, so the block amax is reduced inside the tile (the 16 lanes of a

@@ -92,6 +92,10 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
 // zeros.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;      // 32-bit data format, no swizzle
+// A lane offset no buffer resource here reaches: the launcher keeps every
+// extent (and extent plus k-step offset) below 2^31.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
@@ -149,7 +153,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     const int wm = wave / WNW, wn = wave % WNW;
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
     const int ldw = p.ldw;                          // weight row pitch (elements)
-    const int nk = Kdim / BK;
+    const int nk = (Kdim + BK - 1) / BK;            // the last k-step may be partial (K % 64 != 0)
+    // contraction offset, within a k-step, of the 16-byte chunk this lane
+    // fetches in every direct load (rows of a load's 1 KiB block start at
+    // multiples of 8, so a row's (row & 7) is lane / 8)
+    const int lane_k = swz(lane / 8, lane % 8) * 8;
 
     // largest experts' tiles first; the first row stage is free scratch until the first load
     build_tile_prefix_sorted<NT, BM>(p, s_pre, s_ord, reinterpret_cast<int*>(sa0), s_tmp);
@@ -198,13 +206,16 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
             // the step after the last gets an empty extent: every access out of range
             const rsrc_t r = make_rsrc(is_a ? (const void*)abase : (up ? (const void*)wu : (const void*)wg),
                                        live ? (is_a ? a_bytes : w_bytes) : 0u);
+            // chunks past K (a partial last step) get an offset beyond every
+            // extent, so they read nothing and land zeros in both operands
+            const uint32_t vo = kstep * BK + lane_k < Kdim ? off[i] : kOutOfRange;
             // the row block is re-read by every n-tile of the expert (kept in
             // L2); weight tiles are read by one or two m-tiles close together in
             // tile order, so only the weights stream (non-temporal)
             if (is_a)
-                lds_buf16<0>(r, dst, off[i], kstep * BK * 2);
+                lds_buf16<0>(r, dst, vo, kstep * BK * 2);
             else
-                lds_buf16<kNonTemporal>(r, dst, off[i], kstep * BK * 2);
+                lds_buf16<kNonTemporal>(r, dst, vo, kstep * BK * 2);
         };
 
         // per-lane LDS byte offset of the 16-byte chunk this lane feeds to an

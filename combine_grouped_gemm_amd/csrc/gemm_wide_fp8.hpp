@@ -121,7 +121,6 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
     const int ldw = p.ldw;                          // weight row pitch (bytes = elements)
     const int nk = (Kdim + ROWB - 1) / ROWB;        // k-steps = scale blocks (<= kMaxKBlocks)
-    const bool k_tail = nk * ROWB != Kdim;          // last block holds 64 bytes
     const int nbN = (N + 127) / 128;
 
     // largest experts' tiles first; the first row stage is free scratch until the first load
@@ -225,8 +224,8 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     // next k-step re-reads the second one, which must still be in L2.
     auto issue_p = [&](auto I, int kstep, auto WPOL) {
         const uint32_t kb = (uint32_t)kstep * ROWB;
-        // in a 64-byte tail block, chunks 4..7 come from the zero block
-        const bool zl = k_tail && kstep == nk - 1 && lchunk >= 4;
+        // in a partial last block the chunks past K come from the zero block
+        const bool zl = kstep * ROWB + lchunk * 16 >= Kdim;
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
             const int q = i * NW + wave;

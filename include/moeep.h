@@ -28,7 +28,8 @@
  *   - MOE_ERR_HIP reports a failed kernel launch.  Faults inside a kernel
  *     surface, as always with HIP, at the caller's next synchronisation.
  *   - Sizes: 1 <= K <= E <= 1024; 0 <= e_begin < e_end <= E; B >= 0;
- *     H and I multiples of 64; row base pointers 16-byte aligned.
+ *     H and I multiples of 8 (of 16 when activations are fp8); row base
+ *     pointers 16-byte aligned.
  *   - Calls on one stream run in order; calls that share output or
  *     workspace buffers on different streams race.
  *   - Expert ids outside [0, E) in topk_ids are treated as unrouted slots.

@@ -66,7 +66,11 @@ def test_dispatch_rejects():
     rows = (ctypes.c_int32 * 1)(4)
     P = lambda a: ctypes.cast(a, ctypes.c_void_p)
     assert L.moe_dispatch(P(ptrs), P(rows), 0, 1, 128, p, 2, p, 1, None, 8, None) == 1
-    assert L.moe_dispatch(P(ptrs), P(rows), 1, 1, 100, p, 2, p, 1, None, 8, None) == 1   # H % 64
+    assert L.moe_dispatch(P(ptrs), P(rows), 1, 1, 100, p, 2, p, 1, None, 8, None) == 1   # H % 8
+    assert L.moe_dispatch(P(ptrs), P(rows), 1, 1, 0, p, 2, p, 1, None, 8, None) == 1     # H >= 8
+    # fp8 rows need H % 16 (the fp8 GEMMs move 16-byte pieces)
+    assert L.moe_dispatch(P(ptrs), P(rows), 1, 1, 200, p, 2, p, 2, p, 8, None) == 1
+    assert "multiple of 16" in L.moe_last_error().decode()
     assert L.moe_dispatch(P(ptrs), P(rows), 1, 0, 128, p, 2, p, 2, None, 8, None) == m.MOE_ERR_UNSUPPORTED
     assert L.moe_dispatch(P(ptrs), P(rows), 1, 1, 128, p, 2, p, 2, None, 8, None) == 1   # fp8 needs scales
     ptrs[0] = 4097
@@ -79,8 +83,12 @@ def test_ffn_rejects():
     p = ctypes.c_void_p(4096)
     # bf16 activations with fp8 weights: unsupported
     assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 1, p, p, None, None, 2, p, None, 0, None) == 2
-    # I not a multiple of 64
+    # I not a multiple of 8
     assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 100, 1, p, p, None, None, 1, p, None, 0, None) == 1
+    assert "multiples of 8" in L.moe_last_error().decode()
+    # fp8: H and I multiples of 16
+    assert L.moe_ffn_gate_up(p, p, p, 8, 64, 200, 128, 2, p, p, p, p, 2, p, p, 0, None) == 1
+    assert "multiples of 16" in L.moe_last_error().decode()
     # fp8 without scales
     assert L.moe_ffn_gate_up(p, None, p, 8, 64, 128, 128, 2, p, p, None, None, 2, p, None, 0, None) == 1
     # fp8 activations need a bf16 y
@@ -101,7 +109,7 @@ def test_combine_rejects():
     L = m.lib()
     p = ctypes.c_void_p(4096)
     assert L.moe_combine(p, 2, 8, p, p, 4, 2, 128, p, 1, None) == m.MOE_ERR_UNSUPPORTED
-    assert L.moe_combine(p, 1, 8, p, p, 4, 2, 120, p, 1, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(p, 1, 8, p, p, 4, 2, 124, p, 1, None) == m.MOE_ERR_INVALID_ARG   # H % 8
     assert L.moe_combine(p, 1, 8, None, p, 4, 2, 128, p, 1, None) == m.MOE_ERR_INVALID_ARG
 
 
@@ -128,7 +136,7 @@ def test_masked_entry_points_reject():
     assert "cap_per_expert" in L.moe_last_error().decode()
     assert L.moe_grouped_ffn_masked(p, None, p, 4, 16, 100, 128, 1, p, p, p, None, None, None, 1,
                                     p, 1, p, 1 << 30, 0, None) == m.MOE_ERR_INVALID_ARG
-    assert "multiples of 64" in L.moe_last_error().decode()
+    assert "multiples of 8" in L.moe_last_error().decode()
 
 
 def test_eplb_place_matches_oracle_and_rejects():

@@ -47,6 +47,22 @@ SMALL = [
     wl.scaled(C["dsv3_prefill"], "prefill_many_experts", seg_rows=(4800,), E=600, K=8, H=128, I=64),
     wl.scaled(C["gptoss_fp8"], "fp8_wide_many_experts", seg_rows=(3600,), E=600, K=8, H=256, I=128,
               w_scales="pow2"),
+    # H and I not multiples of 64: a partial last k-step (8 of 64 bf16 / f32 elements at
+    # H = 200, 8 at I = 136; fp8: 80 of 128 bytes at H = 208, 16 at I = 144) and partial
+    # output tiles, through every kernel family: the f32 kernel, the 16- and 128-row
+    # register-staged bf16 tiles, the 256- and 320-row bf16 rings, the 16- and 128-row fp8
+    # tiles and the wide fp8 ring, both weight-scale conventions
+    wl.scaled(C["toy"], "f32_k_tail", seg_rows=(40, 24), E=16, K=2, H=200, I=136),
+    wl.scaled(C["dsv3_decode"], "bf16_16row_k_tail", seg_rows=(40,), E=32, K=4, H=200, I=136),
+    wl.scaled(C["dsv3_decode"], "bf16_128row_k_tail", seg_rows=(300,), E=16, K=2, H=200, I=136),
+    wl.scaled(C["dsv3_prefill"], "bf16_wide256_k_tail", seg_rows=(600,), E=8, K=2, H=200, I=136),
+    wl.scaled(C["dsv3_prefill"], "bf16_wide320_k_tail", seg_rows=(640,), E=4, K=2, H=200, I=136),
+    wl.scaled(C["gptoss_fp8"], "fp8_16row_k_tail", seg_rows=(24,), E=16, K=2, H=208, I=144, w_scales="pow2"),
+    wl.scaled(C["gptoss_fp8"], "fp8_128row_k_tail", seg_rows=(160,), E=16, K=2, H=208, I=144,
+              w_scales="fp32"),
+    wl.scaled(C["gptoss_fp8"], "fp8_wide_k_tail", seg_rows=(400,), E=8, K=2, H=208, I=144, w_scales="fp32"),
+    wl.scaled(C["gptoss_fp8"], "fp8_wide_k_tail_po2", seg_rows=(400,), E=8, K=2, H=208, I=144,
+              w_scales="pow2"),
     # more than 8 slots per token: combine gathers in passes of 8 slots (two and three passes)
     wl.scaled(C["dsv3_decode"], "decode_k12", seg_rows=(48,), E=32, K=12, H=256, I=128),
     wl.scaled(C["dsv3_prefill"], "prefill_k20", seg_rows=(40,), E=64, K=20, H=128, I=64),
