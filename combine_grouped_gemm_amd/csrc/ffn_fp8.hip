@@ -338,10 +338,11 @@ hipError_t launch_wide(const FfnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_ffn_fp8(const FfnArgs& a, bool gated, hipStream_t stream) {
-    // the wide kernel keeps all of a tile's scale blocks in LDS and addresses an
-    // expert's weight matrix with 32-bit offsets
+    // the wide kernel keeps all of a tile's scale blocks in LDS, addresses an
+    // expert's weight matrix with 32-bit offsets and takes a whole or a half
+    // (64-byte) last block
     const int nbK = (a.Kdim + 127) / 128;
-    const bool wide_ok = nbK <= widefp8::kMaxKBlocks &&
+    const bool wide_ok = nbK <= widefp8::kMaxKBlocks && (a.Kdim % 128 == 0 || a.Kdim % 128 == 64) &&
                          (unsigned long long)a.N * a.ldw < (1ull << 32);
     if (wide_ok && a.rows_hint >= 48) {
         if (a.w_scales_pow2)

@@ -29,9 +29,10 @@
 // Lane l feeds row (l % 16) with bytes [32*(l/16), 32*(l/16)+32) of the
 // block for both operands.
 //
-// K need not be a multiple of 128 (K = 2880 leaves a 64-byte tail block): in
-// the tail step the direct loads of chunks past K read a 16-byte zero block
-// instead, so both operands are zero there (a garbage fp8 code could be NaN).
+// K is a multiple of 128 or leaves a 64-byte tail block (K = 2880; other K
+// go through the register-staged tiles): in the tail step the direct loads of
+// chunks 4..7 read a 16-byte zero block instead, so both operands are zero
+// there (a garbage fp8 code could be NaN).
 #pragma once
 
 #include "gemm_wide.hpp"
@@ -74,6 +75,38 @@ __device__ __forceinline__ int stage_scale_run(const float* run, const float* en
     return sh;
 }
 
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) char*)reinterpret_cast<const char*>(p));
+}
+
+// Four 32-byte operand fragments (two 16-byte LDS reads each) read in one
+// block that also waits for them: the reads of a buffer whose next direct
+// loads are issued right after, kept out of the compiler's own wait
+// placement (which, not knowing which loads are still in flight on every
+// path, would wait for all of them first).
+__device__ __forceinline__ void lds_read_frags4(intx8 (&fr)[4], const uint32_t (&ad)[8]) {
+    uint4 t[8];
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+        fr[f] = intx8{(int)t[2 * f].x, (int)t[2 * f].y, (int)t[2 * f].z, (int)t[2 * f].w,
+                      (int)t[2 * f + 1].x, (int)t[2 * f + 1].y, (int)t[2 * f + 1].z, (int)t[2 * f + 1].w};
+}
+
 // Waves laid out WMW (rows) x WNW (weight rows); a wave owns the interleaved
 // 16-row fragments {wm, wm + WMW, ...} and BN / WNW weight rows.
 template <int BM, int BN, int WMW, int WNW, bool GATED, bool PO2W>
@@ -90,6 +123,13 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     static_assert(BM % (16 * WMW) == 0 && BN % (16 * WNW) == 0 && (!GATED || (FN % 2 == 0 && BNO == 128)),
                   "tile shape");
     static_assert(BLOCKS % NW == 0, "every wave issues LPS loads per stage");
+    static_assert(A_BLOCKS % NW == 0, "a wave's first A_LPS loads of a stage are row loads, the rest weight loads");
+    constexpr int A_LPS = A_BLOCKS / NW;
+    constexpr int B_LPS = LPS - A_LPS;
+    // with 8 waves, load i of a stage covers 64 consecutive operand rows and
+    // a lane always fetches row (wave * 8 + lane / 8) of them
+    static_assert(NW == 8, "one 64-row group per load");
+    constexpr int B_OFFS = (GATED ? BN / 2 : BN) / 64;   // distinct weight-row groups (gate and up share)
     static_assert(BM * SK % kWave == 0 && BN * SK % kWave == 0 && BN / 2 * SK % kWave == 0,
                   "scale staging by 64-lane loads");
 
@@ -121,6 +161,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     const int Kdim = p.Kdim, N = p.N, cap = p.cap;
     const int ldw = p.ldw;                          // weight row pitch (bytes = elements)
     const int nk = (Kdim + ROWB - 1) / ROWB;        // k-steps = scale blocks (<= kMaxKBlocks)
+    const bool k_tail = nk * ROWB != Kdim;          // the last block holds 64 bytes (launcher: K % 128 is 0 or 64)
     const int nbN = (N + 127) / 128;
 
     // largest experts' tiles first; the first row stage is free scratch until the first load
@@ -146,7 +187,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     const char* abase = nullptr;
     const char* gbase = nullptr;
     const char* ubase = nullptr;
-    uint32_t off[LPS];
+    uint32_t off_a[A_LPS], off_b[B_OFFS];    // lane offsets of a stage's loads (k-step 0)
     int a_sh = 0, b_sh0 = 0, b_sh1 = 4;
 
     // decode tile t, copy its scales to LDS and set the load state.  Scales go
@@ -202,19 +243,17 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
         abase = reinterpret_cast<const char*>(A + (size_t)row0 * Kdim);
         gbase = reinterpret_cast<const char*>(W0 + (size_t)j * N * ldw);
         ubase = GATED ? reinterpret_cast<const char*>(W1 + (size_t)j * N * ldw) : nullptr;
+        const int lrow = wave * 8 + lane / 8;
+        const uint32_t c16 = (uint32_t)lchunk * 16;
 #pragma unroll
-        for (int i = 0; i < LPS; ++i) {
-            const int q = i * NW + wave;                 // wave-uniform
-            const uint32_t c16 = (uint32_t)lchunk * 16;
-            if (q < A_BLOCKS) {
-                const int r = q * 8 + lane / 8;
-                off[i] = (uint32_t)(r < nvalid ? r : 0) * (uint32_t)Kdim + c16;
-            } else {
-                const int r = (q - A_BLOCKS) * 8 + lane / 8;
-                const int rr = (GATED && r >= BN / 2) ? r - BN / 2 : r;
-                const int col = col0 + rr;
-                off[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)ldw + c16;
-            }
+        for (int i = 0; i < A_LPS; ++i) {
+            const int r = i * 64 + lrow;
+            off_a[i] = (uint32_t)(r < nvalid ? r : 0) * (uint32_t)Kdim + c16;
+        }
+#pragma unroll
+        for (int i = 0; i < B_OFFS; ++i) {
+            const int col = col0 + i * 64 + lrow;
+            off_b[i] = (uint32_t)(col < N ? col : 0) * (uint32_t)ldw + c16;
         }
         return tc;
     };
@@ -222,28 +261,37 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
     // on 128-byte lines (a row pitch that is a multiple of 128, as packed
     // weights have): otherwise a k-step's 128 bytes straddle two lines and the
     // next k-step re-reads the second one, which must still be in L2.
-    auto issue_p = [&](auto I, int kstep, auto WPOL) {
+    auto issue_p = [&](auto I, int kstep, auto WPOL, auto FIRST, auto LAST) {
         const uint32_t kb = (uint32_t)kstep * ROWB;
-        // in a partial last block the chunks past K come from the zero block
-        const bool zl = kstep * ROWB + lchunk * 16 >= Kdim;
+        // in a 64-byte last block, chunks 4..7 come from the zero block
+        const bool zl = k_tail && kstep == nk - 1 && lchunk >= 4;
 #pragma unroll
-        for (int i = 0; i < LPS; ++i) {
-            const int q = i * NW + wave;
-            if (q >= BLOCKS) break;                      // wave-uniform
-            const bool is_a = q < A_BLOCKS;
-            const bool up = GATED && !is_a && (q - A_BLOCKS) * 8 >= BN / 2;
+        for (int i = decltype(FIRST)::value; i < decltype(LAST)::value; ++i) {
+            const int q = i * NW + wave;                 // < BLOCKS: LPS * NW == BLOCKS
+            // operand, gate / up half and row group are known per unrolled load
+            const bool is_a = i < A_LPS;
+            const int ib = i - A_LPS;
+            const bool up = GATED && !is_a && ib * 64 >= BN / 2;
             const char* b = is_a ? abase : (up ? ubase : gbase);
+            const uint32_t o = is_a ? off_a[is_a ? i : 0] : off_b[is_a ? 0 : ib % B_OFFS];
             char* dst = is_a ? a_base(I) + q * 1024 : b_base(I) + (q - A_BLOCKS) * 1024;
-            const char* src = zl ? reinterpret_cast<const char*>(kZeroChunk) : b + off[i] + kb;
+            // 32-bit offset add: a uniform base plus one lane offset per load
+            const char* src = zl ? reinterpret_cast<const char*>(kZeroChunk) : b + (uint32_t)(o + kb);
             if (is_a)
                 wide::lds_dma16<0>(src, dst);
             else
                 wide::lds_dma16<decltype(WPOL)::value>(src, dst);
         }
     };
+    // a k-step's row loads, its weight loads, or both
+    auto issue_a = [&](auto I, int kstep) { issue_p(I, kstep, ic<0>{}, ic<0>{}, ic<A_LPS>{}); };
+    auto issue_b = [&](auto I, int kstep) {
+        if (w_lines) issue_p(I, kstep, ic<wide::kNonTemporal>{}, ic<A_LPS>{}, ic<LPS>{});
+        else issue_p(I, kstep, ic<0>{}, ic<A_LPS>{}, ic<LPS>{});
+    };
     auto issue = [&](auto I, int kstep) {
-        if (w_lines) issue_p(I, kstep, ic<wide::kNonTemporal>{});
-        else issue_p(I, kstep, ic<0>{});
+        issue_a(I, kstep);
+        issue_b(I, kstep);
     };
 
     TileCoord cur{};
@@ -283,13 +331,32 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             const char* bb = b_base(I);
             intx8 bfr[FN];
             float bsc[FN];
+            static_assert(FN == 4, "weight fragment reads");
+            {
+                uint32_t ad[2 * FN];
+#pragma unroll
+                for (int f = 0; f < FN; ++f) {
+                    const int r = brow(f);
+                    ad[2 * f] = lds_addr(bb + r * ROWB + wide::swz(r, c0) * 16);
+                    ad[2 * f + 1] = lds_addr(bb + r * ROWB + wide::swz(r, c0 + 1) * 16);
+                }
+                lds_read_frags4(bfr, ad);
+            }
+            // (issued after this step's fragment reads, which therefore need
+            // not wait for them) step 1's weights on a tile's first step, then
+            // step kstep + 1's rows into the other row buffer
+            if (kstep == 0 && nk > 1) issue_b(ic<1>{}, 1);
+            if (kstep + 1 < nk) issue_a(ic<1 - decltype(I)::value>{}, kstep + 1);
+            // every wave holds this step's weight fragments: their buffer
+            // takes step kstep + 2's weights
+            if (kstep + 2 < nk) {
+                wide::wait_lgkm0();
+                wide::block_barrier();
+                issue_b(I, kstep + 2);
+            }
 #pragma unroll
             for (int f = 0; f < FN; ++f) {
                 const int r = brow(f);
-                const uint4 t0 = *reinterpret_cast<const uint4*>(bb + r * ROWB + wide::swz(r, c0) * 16);
-                const uint4 t1 = *reinterpret_cast<const uint4*>(bb + r * ROWB + wide::swz(r, c0 + 1) * 16);
-                bfr[f] = intx8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w,
-                               (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
                 bsc[f] = s_bs[(r < BN / 2 ? b_sh0 : b_sh1) + r * SK + kstep];
             }
             int sb8[FN];        // weight-row scales as E8M0 bytes (power-of-two weight scales)
@@ -330,14 +397,17 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             }
         };
 
-        // step k: wait for stage k (nothing else is in flight), then load k+1
-        // into the other buffer while computing k
+        // step k: wait for stage k's rows and weights (step k + 1's weights,
+        // issued during step k - 1, stay in flight) and compute it; the
+        // compute loads step k + 1's rows into the other row buffer and, once
+        // every wave holds step k's weight fragments in registers, step k +
+        // 2's weights into their buffer, so the weight stream keeps one to two
+        // k-steps in flight instead of draining at every step.
         auto step = [&](auto I, int k) {
-            constexpr int s = decltype(I)::value;
-            wide::wait_vmcnt<0>();
+            if (k > 0 && k + 1 < nk) wide::wait_vmcnt<B_LPS>();
+            else wide::wait_vmcnt<0>();
             wide::wait_lgkm0();
             wide::block_barrier();
-            if (k + 1 < nk) issue(ic<1 - s>{}, k + 1);
             compute(I, k);
         };
         for (int k = 0; k < nk; k += 2) {

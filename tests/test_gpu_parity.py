@@ -50,8 +50,10 @@ SMALL = [
     # H and I not multiples of 64: a partial last k-step (8 of 64 bf16 / f32 elements at
     # H = 200, 8 at I = 136; fp8: 80 of 128 bytes at H = 208, 16 at I = 144) and partial
     # output tiles, through every kernel family: the f32 kernel, the 16- and 128-row
-    # register-staged bf16 tiles, the 256- and 320-row bf16 rings, the 16- and 128-row fp8
-    # tiles and the wide fp8 ring, both weight-scale conventions
+    # register-staged bf16 tiles, the 256- and 320-row bf16 rings and the 16- and 128-row
+    # fp8 tiles, both weight-scale conventions (the wide fp8 ring takes K % 128 of 0 or 64
+    # only, so the ~100-row fp8 cases here run the 128-row tiles; its 64-byte tail is
+    # covered by the H = 320 / I = 192 and H = I = 2880 cases above)
     wl.scaled(C["toy"], "f32_k_tail", seg_rows=(40, 24), E=16, K=2, H=200, I=136),
     wl.scaled(C["dsv3_decode"], "bf16_16row_k_tail", seg_rows=(40,), E=32, K=4, H=200, I=136),
     wl.scaled(C["dsv3_decode"], "bf16_128row_k_tail", seg_rows=(300,), E=16, K=2, H=200, I=136),
