@@ -71,14 +71,18 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_copy_kernel(
     const int32_t* rows = row_of + (size_t)t * K;
     int my = slot_row(rows, K, 0, cap, lane);
     uint64_t m = ballot64(my >= 0);          // local slots among the first 64, the same in every wave
-    if ((m == 0 && (K <= kWave || !any_local(rows, K, cap, lane))) || c >= nvec) return;
-    const uint4 v = static_cast<const uint4*>(token_row(seg, t, row_bytes))[c];
+    if (m == 0 && (K <= kWave || !any_local(rows, K, cap, lane))) return;
+    // lanes past the row stay: with more than 64 slots each later ballot needs
+    // every lane of the wave (lane l holds slot k0 + l)
+    const bool ok = c < nvec;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (ok) v = static_cast<const uint4*>(token_row(seg, t, row_bytes))[c];
     for (int k0 = 0;;) {
         while (m != 0) {
             const int k = __builtin_ctzll(m);
             m &= m - 1;
             const int r = __builtin_amdgcn_readlane(my, k);
-            reinterpret_cast<uint4*>(xd + (size_t)r * row_bytes)[c] = v;
+            if (ok) reinterpret_cast<uint4*>(xd + (size_t)r * row_bytes)[c] = v;
         }
         k0 += kWave;
         if (k0 >= K) break;
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
     amax = row16_max(amax);
-    if (!ok) return;
+    // lanes past the row stay for the later slot ballots (more than 64 slots)
     const float s = pow2_block_scale(amax);
     const float rs = 1.0f / s;               // exact: s is a power of two
     // |f * rs| <= amax / s <= 448, the range where the hardware conversion is exact RNE
@@ -123,8 +127,10 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_fp8_kernel(
             const int k = __builtin_ctzll(m);
             m &= m - 1;
             const int r = __builtin_amdgcn_readlane(my, k);
-            reinterpret_cast<uint2*>(xd + (size_t)r * H)[c] = make_uint2(lo, hi);
-            if ((c & 15) == 0) xd_scales[(size_t)r * nblk + c / 16] = s;
+            if (ok) {
+                reinterpret_cast<uint2*>(xd + (size_t)r * H)[c] = make_uint2(lo, hi);
+                if ((c & 15) == 0) xd_scales[(size_t)r * nblk + c / 16] = s;
+            }
         }
         k0 += kWave;
         if (k0 >= K) break;

@@ -70,6 +70,11 @@ SMALL = [
     wl.scaled(C["dsv3_prefill"], "prefill_k20", seg_rows=(40,), E=64, K=20, H=128, I=64),
     # more than 64 slots per token: dispatch and combine read the slot rows 64 at a time
     wl.scaled(C["dsv3_decode"], "decode_k70", seg_rows=(20,), E=128, K=70, H=128, I=64),
+    # slots past 64 + 16 and past 64 + 40 with rows of 16 (bf16 H = 128) and 40 (fp8
+    # H = 320) vectors: the lanes past the row hold those slots in the second ballot
+    wl.scaled(C["dsv3_decode"], "decode_k100_partial_wave", seg_rows=(12,), E=128, K=100, H=128, I=64),
+    wl.scaled(C["gptoss_fp8"], "fp8_k120_partial_wave", seg_rows=(6,), E=128, K=120, H=320, I=192,
+              w_scales="pow2"),
     # the single-workgroup layout's limit: 4096 slots (four 1024-slot chunks) and just past
     # it (the three-kernel layout), on a partial expert range
     wl.scaled(C["ep8_share"], "layout_4096_slots", seg_rows=(300, 212), E=32, K=8, H=128, I=64,
