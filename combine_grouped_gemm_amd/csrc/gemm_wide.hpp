@@ -110,6 +110,33 @@ __device__ __forceinline__ void lds_buf16(rsrc_t r, void* lds_wave_base, uint32_
 #endif
 }
 
+// Eight 16-byte LDS reads in one block that also waits for them: operand
+// fragments of a buffer whose loads for a later step are issued right
+// after, kept out of the compiler's own wait placement (which, not knowing
+// on every path which direct loads are still in flight, waits for all of
+// them before the first read).
+__device__ __forceinline__ void lds_read16x8(uint4 (&t)[8], const uint32_t (&ad)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) char*)reinterpret_cast<const char*>(p));
+}
+
 // 8 waves laid out 2 (rows) x 4 (weight rows).  A wave owns the interleaved
 // 16-row fragments {wm, wm + 2, ...} (so a short tile still spreads its valid
 // rows over both row-waves) and 64 weight rows.
@@ -129,6 +156,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     static_assert(A_BLOCKS % NW == 0 && (BN / 16) % NW == 0, "block split");
     constexpr int A_ITERS = A_BLOCKS / NW;           // i < A_ITERS: row blocks
     constexpr int G_ITERS = (BN / 16) / NW;          // next G_ITERS: gate (or first) weight half
+    constexpr int B_ITERS = LPS - A_ITERS;           // weight loads per wave per stage
+    // Tiles of at most 256 rows keep both k-halves' weight fragments of a step
+    // in registers, so the weight buffer of step k takes step k + 2's weights
+    // as soon as every wave holds them (the weight stream keeps up to two
+    // steps in flight); 320-row tiles have no registers to spare for that.
+    constexpr bool LOOK = BM <= 256;
 
     __shared__ uint4 sa0[BM * CPR];
     __shared__ uint4 sb0[BN * CPR];
@@ -250,6 +283,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
         block_barrier();
 #pragma unroll
         for (int i = 0; i < LPS; ++i) issue_one(ic<0>{}, i, 0, true);
+        if constexpr (LOOK) {
+            // and step 1's weights (nothing read when there is no step 1)
+            const bool l1 = __builtin_amdgcn_readfirstlane(nk > 1 ? 1 : 0) != 0;
+#pragma unroll
+            for (int i = A_ITERS; i < LPS; ++i) issue_one(ic<1>{}, i, 1, l1);
+        }
 
         // The tile for NF valid fragments: no branch inside a step.
         // v_mfma_f32_16x16x32_bf16: lane l feeds row (l % 16) with k-chunk (l / 16)
@@ -302,16 +341,77 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
                 }
             };
 
-            // step k: wait for stage k (nothing else is in flight), then compute
-            // k while stage k + 1 is loaded into the other buffer
+            // LOOK: read both k-halves' weight fragments of step k, and once every
+            // wave holds them issue, one after each fragment's MFMA group, step
+            // k + 1's row loads into the other row buffer and then step k + 2's
+            // weight loads into this step's weight buffer (loads past the last
+            // step read nothing but count, so every step issues LPS loads)
+            auto compute_look = [&](auto I, int k, bool liveA, bool liveB) {
+                const char* ab = a_base(I);
+                const char* bb = b_base(I);
+                constexpr auto nextbuf = ic<1 - decltype(I)::value>{};
+                static_assert(2 * FN == 8, "weight fragment reads");
+                bf16x8 bfr[2][FN];
+                {
+                    uint32_t ad[8];
+                    uint4 t[8];
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int f = 0; f < FN; ++f) ad[kk * FN + f] = lds_addr(bb + lds_lane[kk] + brow0(f) * ROWB);
+                    lds_read16x8(t, ad);
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int f = 0; f < FN; ++f) bfr[kk][f] = __builtin_bit_cast(bf16x8, t[kk * FN + f]);
+                }
+                block_barrier();
+                auto issue_slot = [&](int q) {
+                    if (q < A_ITERS) issue_one(nextbuf, q, k + 1, liveA);
+                    else issue_one(I, q, k + 2, liveB);
+                };
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 acur;
+                    if (NF > 0) acur = *reinterpret_cast<const bf16x8*>(ab + lds_lane[kk] + wm * 16 * ROWB);
+#pragma unroll
+                    for (int i = 0; i < NF; ++i) {
+                        bf16x8 anext;
+                        if (i + 1 < NF)
+                            anext = *reinterpret_cast<const bf16x8*>(
+                                ab + lds_lane[kk] + (wm + WMW * (i + 1)) * 16 * ROWB);
+#pragma unroll
+                        for (int f = 0; f < FN; ++f)
+                            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur, bfr[kk][f], acc[i][f], 0, 0, 0);
+                        const int slot = kk * NF + i;
+                        if (slot < LPS) issue_slot(slot);
+                        if (i + 1 < NF) acur = anext;
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                if (2 * NF < LPS) {
+#pragma unroll
+                    for (int q = 2 * NF; q < LPS; ++q) issue_slot(q);
+                }
+            };
+
+            // step k: wait for stage k (nothing else is in flight; LOOK: step
+            // k + 1's weights stay in flight), then compute k while stage k + 1
+            // is loaded into the other buffer
             auto step = [&](auto I, int k) {
-                wait_vmcnt<0>();
+                if constexpr (LOOK) wait_vmcnt<B_ITERS>();
+                else wait_vmcnt<0>();
                 wait_lgkm0();
                 block_barrier();
                 // wave-uniform by construction; say so, so that the resource
                 // select below stays scalar
                 const bool live = __builtin_amdgcn_readfirstlane(k + 1 < nk ? 1 : 0) != 0;
-                compute(I, k + 1, live);
+                if constexpr (LOOK) {
+                    const bool live2 = __builtin_amdgcn_readfirstlane(k + 2 < nk ? 1 : 0) != 0;
+                    compute_look(I, k, live, live2);
+                } else {
+                    compute(I, k + 1, live);
+                }
             };
             for (int k = 0; k < nk; k += 2) {
                 step(ic<0>{}, k);

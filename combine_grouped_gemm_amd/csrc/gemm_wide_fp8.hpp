@@ -75,38 +75,6 @@ __device__ __forceinline__ int stage_scale_run(const float* run, const float* en
     return sh;
 }
 
-// 32-bit LDS address of a pointer into a __shared__ array
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)reinterpret_cast<uintptr_t>(
-        (const __attribute__((address_space(3))) char*)reinterpret_cast<const char*>(p));
-}
-
-// Four 32-byte operand fragments (two 16-byte LDS reads each) read in one
-// block that also waits for them: the reads of a buffer whose next direct
-// loads are issued right after, kept out of the compiler's own wait
-// placement (which, not knowing which loads are still in flight on every
-// path, would wait for all of them first).
-__device__ __forceinline__ void lds_read_frags4(intx8 (&fr)[4], const uint32_t (&ad)[8]) {
-    uint4 t[8];
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %10\n\t"
-        "ds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %13\n\t"
-        "ds_read_b128 %6, %14\n\t"
-        "ds_read_b128 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
-        : "memory");
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-        fr[f] = intx8{(int)t[2 * f].x, (int)t[2 * f].y, (int)t[2 * f].z, (int)t[2 * f].w,
-                      (int)t[2 * f + 1].x, (int)t[2 * f + 1].y, (int)t[2 * f + 1].z, (int)t[2 * f + 1].w};
-}
-
 // Waves laid out WMW (rows) x WNW (weight rows); a wave owns the interleaved
 // 16-row fragments {wm, wm + WMW, ...} and BN / WNW weight rows.
 template <int BM, int BN, int WMW, int WNW, bool GATED, bool PO2W>
@@ -334,13 +302,18 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             static_assert(FN == 4, "weight fragment reads");
             {
                 uint32_t ad[2 * FN];
+                uint4 t[2 * FN];
 #pragma unroll
                 for (int f = 0; f < FN; ++f) {
                     const int r = brow(f);
-                    ad[2 * f] = lds_addr(bb + r * ROWB + wide::swz(r, c0) * 16);
-                    ad[2 * f + 1] = lds_addr(bb + r * ROWB + wide::swz(r, c0 + 1) * 16);
+                    ad[2 * f] = wide::lds_addr(bb + r * ROWB + wide::swz(r, c0) * 16);
+                    ad[2 * f + 1] = wide::lds_addr(bb + r * ROWB + wide::swz(r, c0 + 1) * 16);
                 }
-                lds_read_frags4(bfr, ad);
+                wide::lds_read16x8(t, ad);
+#pragma unroll
+                for (int f = 0; f < FN; ++f)
+                    bfr[f] = intx8{(int)t[2 * f].x, (int)t[2 * f].y, (int)t[2 * f].z, (int)t[2 * f].w,
+                                   (int)t[2 * f + 1].x, (int)t[2 * f + 1].y, (int)t[2 * f + 1].z, (int)t[2 * f + 1].w};
             }
             // (issued after this step's fragment reads, which therefore need
             // not wait for them) step 1's weights on a tile's first step, then
