@@ -131,6 +131,18 @@ __device__ __forceinline__ void lds_read16x8(uint4 (&t)[8], const uint32_t (&ad)
         : "memory");
 }
 
+__device__ __forceinline__ void lds_read16x4(uint4 (&t)[4], const uint32_t (&ad)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+}
+
 // 32-bit LDS address of a pointer into a __shared__ array
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>(
@@ -162,6 +174,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
     // as soon as every wave holds them (the weight stream keeps up to two
     // steps in flight); 320-row tiles have no registers to spare for that.
     constexpr bool LOOK = BM <= 256;
+    // wider tiles release the weight buffer half-way: step k + 2's weights go
+    // out during the second k-half, once every wave holds its fragments
+    constexpr bool HALF = !LOOK;
 
     __shared__ uint4 sa0[BM * CPR];
     __shared__ uint4 sb0[BN * CPR];
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
         block_barrier();
 #pragma unroll
         for (int i = 0; i < LPS; ++i) issue_one(ic<0>{}, i, 0, true);
-        if constexpr (LOOK) {
+        if constexpr (LOOK || HALF) {
             // and step 1's weights (nothing read when there is no step 1)
             const bool l1 = __builtin_amdgcn_readfirstlane(nk > 1 ? 1 : 0) != 0;
 #pragma unroll
@@ -395,11 +410,59 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
                 }
             };
 
+            // HALF: as compute, but the first k-half issues step k + 1's row
+            // loads and the second half, once every wave holds its weight
+            // fragments, step k + 2's weight loads into this step's buffer
+            auto compute_half = [&](auto I, int k, bool liveA, bool liveB) {
+                const char* ab = a_base(I);
+                const char* bb = b_base(I);
+                constexpr auto nextbuf = ic<1 - decltype(I)::value>{};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 bfr[FN];
+                    {
+                        static_assert(FN == 4, "weight fragment reads");
+                        uint32_t ad[4];
+                        uint4 t[4];
+#pragma unroll
+                        for (int f = 0; f < FN; ++f) ad[f] = lds_addr(bb + lds_lane[kk] + brow0(f) * ROWB);
+                        lds_read16x4(t, ad);
+#pragma unroll
+                        for (int f = 0; f < FN; ++f) bfr[f] = __builtin_bit_cast(bf16x8, t[f]);
+                    }
+                    if (kk == 1) block_barrier();      // every wave holds this step's weight fragments
+                    bf16x8 acur;
+                    if (NF > 0) acur = *reinterpret_cast<const bf16x8*>(ab + lds_lane[kk] + wm * 16 * ROWB);
+#pragma unroll
+                    for (int i = 0; i < NF; ++i) {
+                        bf16x8 anext;
+                        if (i + 1 < NF)
+                            anext = *reinterpret_cast<const bf16x8*>(
+                                ab + lds_lane[kk] + (wm + WMW * (i + 1)) * 16 * ROWB);
+#pragma unroll
+                        for (int f = 0; f < FN; ++f)
+                            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur, bfr[f], acc[i][f], 0, 0, 0);
+                        if (kk == 0 && i < A_ITERS) issue_one(nextbuf, i, k + 1, liveA);
+                        if (kk == 1 && i < B_ITERS) issue_one(I, A_ITERS + i, k + 2, liveB);
+                        if (i + 1 < NF) acur = anext;
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (kk == 0 && NF < A_ITERS) {
+#pragma unroll
+                        for (int q = NF; q < A_ITERS; ++q) issue_one(nextbuf, q, k + 1, liveA);
+                    }
+                    if (kk == 1 && NF < B_ITERS) {
+#pragma unroll
+                        for (int q = NF; q < B_ITERS; ++q) issue_one(I, A_ITERS + q, k + 2, liveB);
+                    }
+                }
+            };
+
             // step k: wait for stage k (nothing else is in flight; LOOK: step
             // k + 1's weights stay in flight), then compute k while stage k + 1
             // is loaded into the other buffer
             auto step = [&](auto I, int k) {
-                if constexpr (LOOK) wait_vmcnt<B_ITERS>();
+                if constexpr (LOOK || HALF) wait_vmcnt<B_ITERS>();
                 else wait_vmcnt<0>();
                 wait_lgkm0();
                 block_barrier();
@@ -409,6 +472,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
                 if constexpr (LOOK) {
                     const bool live2 = __builtin_amdgcn_readfirstlane(k + 2 < nk ? 1 : 0) != 0;
                     compute_look(I, k, live, live2);
+                } else if constexpr (HALF) {
+                    const bool live2 = __builtin_amdgcn_readfirstlane(k + 2 < nk ? 1 : 0) != 0;
+                    compute_half(I, k, live, live2);
                 } else {
                     compute(I, k + 1, live);
                 }
