@@ -486,22 +486,52 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_wide_kernel(FfnArgs 
             // the loads issued by the last step read nothing but still count
             wait_vmcnt<0>();
 
-            // ---- epilogue
+            // ---- epilogue: every wave stages its bf16 outputs in a private LDS
+            // region (both stages are free once every wave is past the k-loop)
+            // and stores whole 16-byte row chunks: 8 per 128-byte output row
+            // piece instead of one 2-byte store per element.  PF fragments
+            // per pass; staged rows are padded by 16 bytes so that the four
+            // row groups of one LDS write fall into different banks.
             constexpr int FO = GATED ? FN / 2 : FN;
+            constexpr int OCOLS = FO * 16;                  // output columns of a wave
+            constexpr int OCH = OCOLS * 2 / 16;             // 16-byte chunks per staged row
+            constexpr int OPITCH = OCOLS * 2 + 16;          // staged row pitch (bytes)
+            constexpr int PF = 5;                           // fragments per pass
+            constexpr int RSZ = PF * 16 * OPITCH;           // bytes of a wave's region
+            static_assert(2 * RSZ <= BN * ROWB && 2 * RSZ <= BM * ROWB, "two regions per stage buffer");
+            wait_lgkm0();
+            block_barrier();
+            char* region = (wave < 2 ? reinterpret_cast<char*>(sa0) : wave < 4 ? reinterpret_cast<char*>(sb0)
+                            : wave < 6 ? reinterpret_cast<char*>(sa1) : reinterpret_cast<char*>(sb1)) + (wave & 1) * RSZ;
+            const int colbase = fcol(0);                    // the wave's first output column
+            char* out_bytes = reinterpret_cast<char*>(Out);
 #pragma unroll
-            for (int i = 0; i < NF; ++i) {
-                const int mrow = (wm + WMW * i) * 16;
+            for (int p0 = 0; p0 < NF; p0 += PF) {
 #pragma unroll
-                for (int f = 0; f < FO; ++f) {
-                    const int col = fcol(f) + (lane & 15);
-                    if (col >= N) continue;
+                for (int ii = 0; ii < PF; ++ii) {
+                    const int i = p0 + ii;
+                    if (i < NF) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = mrow + (lane >> 4) * 4 + e;
-                        if (r < nvalid) {
-                            const float val = GATED ? silu(acc[i][f][e]) * acc[i][f + FN / 2][e] : acc[i][f][e];
-                            Out[(size_t)(row0 + r) * N + col] = (uint16_t)f32_to_bf16_bits(val);
-                        }
+                        for (int f = 0; f < FO; ++f)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float val = GATED ? silu(acc[i][f][e]) * acc[i][f + FN / 2][e] : acc[i][f][e];
+                                const int lrow = ii * 16 + (lane >> 4) * 4 + e;
+                                *reinterpret_cast<uint16_t*>(region + lrow * OPITCH + (f * 16 + (lane & 15)) * 2) =
+                                    (uint16_t)f32_to_bf16_bits(val);
+                            }
+                    }
+                }
+                constexpr int RPI = 64 / OCH;               // staged rows per 64-lane read
+#pragma unroll
+                for (int q = 0; q < PF * 16 / RPI; ++q) {
+                    const int lrow = q * RPI + lane / OCH, ch = lane % OCH;
+                    const int i = p0 + lrow / 16;
+                    const int trow = (wm + WMW * i) * 16 + lrow % 16;   // row within the tile
+                    const int col = colbase + ch * 8;
+                    if (i < NF && trow < nvalid && col < N) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(region + lrow * OPITCH + ch * 16);
+                        *reinterpret_cast<uint4*>(out_bytes + ((size_t)(row0 + trow) * N + col) * 2) = v;
                     }
                 }
             }
