@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             float* s_amax = reinterpret_cast<float*>(sb1);
             // the h tile (BM rows x 128 bytes) is assembled in the row buffer
             // and leaves as 16-byte row chunks; chunk c of row r sits at chunk
-            // c ^ ((r / 4) % 8), so the four row groups of one byte write fall
+            // c ^ (r % 8), so the eight rows of one half-wave dword write fall
             // into distinct banks
             uint8_t* h_tile = reinterpret_cast<uint8_t*>(sa1);
             // row scales of h, stored with the tile (no global store inside the
@@ -452,21 +452,36 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             wide::wait_lgkm0();
             wide::block_barrier();
             static_assert(FO == 2 && WN / 2 == 32, "two 16-column chunks per wave and fragment row");
+            // A lane holds the codes of one column in each of the wave's two
+            // chunks for four rows; a 4 x 4 byte transpose inside each quad
+            // (partners lane ^ 2, then lane ^ 1: a DPP move and a byte permute
+            // each) leaves lane j of the quad with four consecutive columns of
+            // row j, written as one dword per chunk.
+            const int qj = lane & 3;
+            const uint32_t selA = qj < 2 ? 0x05040100u : 0x03020706u;    // keep low / high half
+            const uint32_t selB = (qj & 1) == 0 ? 0x06020400u : 0x03070105u;
+            auto quad_transpose = [&](uint32_t v) {
+                const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+                const uint32_t a2 = __builtin_amdgcn_perm(x, v, selA);
+                const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a2, 0xB1, 0xF, 0xF, false);
+                return __builtin_amdgcn_perm(y, a2, selB);
+            };
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int mrow = (wm + WMW * i) * 16;
-                if (mrow >= nvalid) continue;
-                const int key = ((mrow >> 2) + (lane >> 4)) & 7;         // (r / 4) % 8 of this lane's rows
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = mrow + (lane >> 4) * 4 + e;
-                    const float rs = s_hrs[r];
-                    // |h| <= amax <= 448 s: the hardware conversion needs no saturation
-                    const uint32_t two = e4m3_pair(hv[i][0][e] * rs, hv[i][1][e] * rs);
-                    uint8_t* row = h_tile + r * ROWB + (lane & 15);
-                    row[((2 * wn) ^ key) * 16] = (uint8_t)two;
-                    row[((2 * wn + 1) ^ key) * 16] = (uint8_t)(two >> 8);
-                }
+                if (mrow >= nvalid) continue;                            // wave-uniform
+                const int rb = mrow + (lane >> 4) * 4;                   // this lane's first row
+                const float4 rs = *reinterpret_cast<const float4*>(s_hrs + rb);
+                // |h| <= amax <= 448 s: the hardware conversion needs no saturation
+                uint32_t p0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hv[i][0][0] * rs.x, hv[i][0][1] * rs.y, 0, false);
+                p0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hv[i][0][2] * rs.z, hv[i][0][3] * rs.w, (int)p0, true);
+                uint32_t p1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hv[i][1][0] * rs.x, hv[i][1][1] * rs.y, 0, false);
+                p1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hv[i][1][2] * rs.z, hv[i][1][3] * rs.w, (int)p1, true);
+                const uint32_t t0 = quad_transpose(p0), t1 = quad_transpose(p1);
+                const int r = rb + qj;
+                uint8_t* row = h_tile + r * ROWB + (lane & 12);             // dword (lane % 16) / 4 of a chunk
+                *reinterpret_cast<uint32_t*>(row + ((2 * wn) ^ (r & 7)) * 16) = t0;
+                *reinterpret_cast<uint32_t*>(row + ((2 * wn + 1) ^ (r & 7)) * 16) = t1;
             }
             wide::wait_lgkm0();
             wide::block_barrier();
@@ -476,25 +491,57 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
             for (int t = tid; t < nvalid * 8; t += NT) {
                 const int r = t >> 3, c = t & 7;
                 if (c < nchunk) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(h_tile + r * ROWB + ((c ^ ((r >> 2) & 7)) * 16));
+                    const uint4 v = *reinterpret_cast<const uint4*>(h_tile + r * ROWB + ((c ^ (r & 7)) * 16));
                     *reinterpret_cast<uint4*>(Out + (size_t)(row0 + r) * N + col0 + c * 16) = v;
                 }
             }
             for (int r = tid; r < nvalid; r += NT) p.out_scales[(size_t)(row0 + r) * nbN + nt] = s_hscale[r];
         } else {
-            uint16_t* Out = static_cast<uint16_t*>(p.out);
+            // bf16 outputs: every wave stages its 64 columns in a private region
+            // of the second stage's buffers (the first already receives the next
+            // tile's loads) and stores whole 16-byte row chunks, 8 per 128-byte
+            // output row piece, instead of one 2-byte store per element.  PF
+            // fragments per pass; staged rows are padded by 16 bytes so that the
+            // four row groups of one LDS write fall into different banks.  The
+            // regions are private, so the passes need no barrier: one wave's LDS
+            // accesses take effect in order.
+            constexpr int OCOLS = FN * 16;                  // output columns of a wave
+            constexpr int OCH = OCOLS * 2 / 16;             // 16-byte chunks per staged row
+            constexpr int OPITCH = OCOLS * 2 + 16;          // staged row pitch (bytes)
+            constexpr int PF = 2;                           // fragments per pass
+            constexpr int RSZ = PF * 16 * OPITCH;           // bytes of a wave's region
+            constexpr int NRA = (int)sizeof(sa1) / RSZ;     // regions in the row buffer
+            static_assert(NRA + (int)sizeof(sb1) / RSZ >= NW, "a region per wave");
+            char* region = wave < NRA ? reinterpret_cast<char*>(sa1) + wave * RSZ
+                                      : reinterpret_cast<char*>(sb1) + (wave - NRA) * RSZ;
+            const int colbase = fcol(0);                    // the wave's first output column
+            char* out_bytes = static_cast<char*>(p.out);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int mrow = (wm + WMW * i) * 16;
-                if (mrow >= nvalid) continue;
+            for (int p0 = 0; p0 < FM; p0 += PF) {
 #pragma unroll
-                for (int f = 0; f < FN; ++f) {
-                    const int col = fcol(f) + (lane & 15);
-                    if (col >= N) continue;
+                for (int ii = 0; ii < PF; ++ii) {
+                    const int i = p0 + ii;
+                    if (i < FM) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = mrow + (lane >> 4) * 4 + e;
-                        if (r < nvalid) Out[(size_t)(row0 + r) * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][f][e]);
+                        for (int f = 0; f < FN; ++f)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int lrow = ii * 16 + (lane >> 4) * 4 + e;
+                                *reinterpret_cast<uint16_t*>(region + lrow * OPITCH + (f * 16 + (lane & 15)) * 2) =
+                                    (uint16_t)f32_to_bf16_bits(acc[i][f][e]);
+                            }
+                    }
+                }
+                constexpr int RPI = 64 / OCH;               // staged rows per 64-lane read
+#pragma unroll
+                for (int q = 0; q < PF * 16 / RPI; ++q) {
+                    const int lrow = q * RPI + lane / OCH, ch = lane % OCH;
+                    const int i = p0 + lrow / 16;
+                    const int trow = (wm + WMW * i) * 16 + lrow % 16;   // row within the tile
+                    const int col = colbase + ch * 8;                   // N is a multiple of 16
+                    if (i < FM && trow < nvalid && col < N) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(region + lrow * OPITCH + ch * 16);
+                        *reinterpret_cast<uint4*>(out_bytes + ((size_t)(row0 + trow) * N + col) * 2) = v;
                     }
                 }
             }
