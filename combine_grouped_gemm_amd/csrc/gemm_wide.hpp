@@ -32,10 +32,14 @@
 // Measured limits on MI355X that shaped this: per k-step the loads of the
 // next stage (32 KB of weights from HBM, 32-40 KB of rows from L2) take about
 // as long as the MFMA work of the current one, and the two waves that share a
-// SIMD finish their MFMA groups about 1000 cycles apart.  Issuing the next
-// stage before waiting for the current one (two stages in flight, with a
-// second barrier per step), loads in the order weights first, and two loads
-// per fragment were each measured slower; deeper rings do not fit in LDS.
+// SIMD finish their MFMA groups about 1000 cycles apart.  The weight stream
+// therefore runs two steps ahead: once every wave holds a step's weight
+// fragments in registers (256-row tiles: both k-halves at the start of the
+// step; 320-row tiles, which lack the registers: the second k-half), a
+// barrier releases that weight buffer and step k + 2's weights go into it.
+// Issuing a whole stage before waiting for the previous one, loads in the
+// order weights first, and two loads per fragment were each measured slower;
+// deeper rings do not fit in LDS.
 #pragma once
 
 #include <type_traits>

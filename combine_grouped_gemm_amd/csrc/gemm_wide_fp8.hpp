@@ -3,10 +3,12 @@
 // used by ffn_fp8.hip.
 //
 // Same ragged persistent tile walk and direct global-to-LDS two-stage ring as
-// the wide bf16 kernel (every step waits for all loads in flight); one k-step
-// is one 128-byte scale block, so the LDS row geometry (8 swizzled 16-byte
-// chunks per row) is identical.  The next tile's scales and first k-step are
-// loaded while the current tile's epilogue runs.  A tile is
+// the wide bf16 kernel: a step's row loads go out one step ahead and its
+// weight loads two steps ahead (a weight buffer is refilled as soon as every
+// wave holds its fragments); one k-step is one 128-byte scale block, so the
+// LDS row geometry (8 swizzled 16-byte chunks per row) is identical.  The
+// next tile's scales and first k-step are loaded while the current tile's
+// epilogue runs.  A tile is
 // up to 192 rows of one expert by 256 weight rows (gate/up: 128 gate + 128
 // up rows of the same output columns, so one tile owns exactly one
 // 128-column block of h and can quantise it in its epilogue).  With 192 rows
