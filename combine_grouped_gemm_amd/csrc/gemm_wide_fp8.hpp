@@ -296,6 +296,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
         };
 
         const int c0 = 2 * (lane >> 4);                 // first logical chunk this lane feeds
+        // a wave whose output columns all lie past N (the last n-tile of an
+        // expert when N is not a multiple of the tile width) skips its MFMAs
+        const bool wcols = fcol(0) < N;
         auto compute = [&](auto I, int kstep) {
             const char* ab = a_base(I);
             const char* bb = b_base(I);
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int mrow = (wm + WMW * i) * 16;
-                if (mrow < nvalid) {
+                if (mrow < nvalid && wcols) {
                     const int r = mrow + (lane & 15);
                     const uint4 t0 = *reinterpret_cast<const uint4*>(ab + r * ROWB + wide::swz(r, c0) * 16);
                     const uint4 t1 = *reinterpret_cast<const uint4*>(ab + r * ROWB + wide::swz(r, c0 + 1) * 16);
@@ -427,8 +430,12 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void grouped_gemm_fp8_wide_kerne
                 for (int f = 0; f < FO; ++f)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const bool ok = fcol(f) < N;        // wave-uniform: N is a multiple of 16
-                        const float h = ok ? silu(acc[i][f][e]) * acc[i][f + FO][e] : 0.f;
+                        // computed for every column and zeroed past N (a select, not
+                        // a branch per element, so the exponentials and reciprocals of
+                        // different elements interleave); columns past N hold finite
+                        // values, their weight rows having re-read row 0
+                        const float hs = silu(acc[i][f][e]) * acc[i][f + FO][e];
+                        const float h = fcol(f) < N ? hs : 0.f;
                         hv[i][f][e] = h;
                         rmax[i][e] = fmaxf(rmax[i][e], fabsf(h));
                     }
